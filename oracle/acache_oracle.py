@@ -1,0 +1,226 @@
+"""Plain fp64 CPU oracle for the ACache slot-mapped attention engine.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports or calls it, and this
+module imports nothing from the product path.
+
+Source: "Affix Cache for Diffusion Large Language Models" (ACache), arXiv
+2608.26140.  Every function states the passage it follows.  Each one is
+written for a reader to check against the paper by eye: explicit per-slot
+gathers, one (layer, head) at a time, a numpy matmul as the only library
+primitive for the dot products, no blocking or fusion.
+
+Readings taken where the paper leaves a step open (all listed in the
+design notes with their reasons):
+  * Eq. (4) normalises over the affix keys only (its softmax argument is
+    Q_mask K_affix^T), so every masked row's affix mass sums to one.
+  * The probe forms O_aff and LSE_aff for every non-affix row (the probe
+    forward, cost O(N H P L) in Section 3.2); only the initially masked rows
+    contribute to s_j.
+  * Heads are query heads; under grouped-query attention query head h reads
+    KV head h // (Hq / Hkv).
+  * K = ceil(rate * L) (with a 1e-9 guard), clamped to [0, L].
+  * Top-K ties go to the lower affix offset; anchors are returned as
+    ascending logical positions.
+  * Private slot i of a request is assigned in ascending logical order of
+    the recompute set R = A u (non-affix positions).
+"""
+import math
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# input decoding (bf16 bit patterns or fp32 values -> fp64, exactly)
+# ----------------------------------------------------------------------------
+def decode(x):
+    """fp64 view of stored values.  uint16/int16 arrays are bf16 bit patterns:
+    a bf16 number is the upper half of the fp32 with the same bits, so the
+    widening is exact."""
+    x = np.asarray(x)
+    if x.dtype in (np.uint16, np.int16):
+        u = x.view(np.uint16).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# anchor count (Section 5, Default Settings: anchor ratios {0, .1, .2, .3, .5, 1})
+# ----------------------------------------------------------------------------
+def anchor_count(L, rate):
+    """Number of Anchor Tokens for an affix of L tokens at anchor ratio `rate`:
+    ceil(rate * L), guarded against rate*L landing a hair above an integer,
+    clamped to [0, L].  Rate 0 is direct reuse, rate 1 full recomputation
+    (Section 5.1)."""
+    if not (0.0 <= rate <= 1.0):
+        raise ValueError("rate must lie in [0, 1]")
+    k = math.ceil(rate * L - 1e-9)
+    return max(0, min(L, k))
+
+
+# ----------------------------------------------------------------------------
+# paged KV access (Section 4.1: paged physical slots; slot s = page s // ps,
+# offset s % ps)
+# ----------------------------------------------------------------------------
+def slot_rows(pool_layer, slots, kv_head, page_size):
+    """Gather one KV head's rows for a list of physical slots, one slot at a
+    time.  pool_layer: [n_pages][Hkv][page_size][d] (stored values)."""
+    d = pool_layer.shape[-1]
+    out = np.empty((len(slots), d), np.float64)
+    for i, s in enumerate(slots):
+        s = int(s)
+        out[i] = decode(pool_layer[s // page_size, kv_head, s % page_size])
+    return out
+
+
+def kv_head_of(h, n_q_heads, n_kv_heads):
+    return h // (n_q_heads // n_kv_heads)
+
+
+def softmax_rows(S):
+    """Row softmax with its log-sum-exp; returns (P, lse)."""
+    m = S.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(S - m).sum(axis=1))
+    return np.exp(S - lse[:, None]), lse
+
+
+# ----------------------------------------------------------------------------
+# one-shot anchor probe: Section 3.2, Eqs. (4) and (5)
+# ----------------------------------------------------------------------------
+def probe_layer(q_layer, k_layer, v_layer, shared_slots, page_size, n_kv_heads,
+                masked_rows, masked_offsets, scale, want_out=True):
+    """One layer of the probe.
+
+    q_layer: [rows][Hq][d] queries of every non-affix row of the batch.
+    k_layer, v_layer: [n_pages][Hkv][ps][d] pool of this layer.
+    shared_slots: [L] physical slot of affix offset j (the shared region).
+    masked_rows / masked_offsets: rows of request b that were masked at the
+    start (M_T) are masked_rows[masked_offsets[b]:masked_offsets[b+1]].
+
+    Returns O_aff [rows][Hq][d], LSE_aff [rows][Hq] (natural log) and the
+    layer's contribution to s_j, [B][L]: sum over query heads and masked rows
+    of the Eq. (4) weights a_{j,k} = softmax_j(q_k . k_j * scale).
+    """
+    rows, Hq, d = q_layer.shape
+    L = len(shared_slots)
+    B = len(masked_offsets) - 1
+    o = np.zeros((rows, Hq, d)) if want_out else None
+    lse = np.zeros((rows, Hq))
+    s = np.zeros((B, L))
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, n_kv_heads)
+        Kaff = slot_rows(k_layer, shared_slots, g, page_size)      # [L][d]
+        Vaff = slot_rows(v_layer, shared_slots, g, page_size)
+        Q = decode(q_layer[:, h, :])                                  # [rows][d]
+        A, lse[:, h] = softmax_rows((Q @ Kaff.T) * scale)             # Eq. (4), every probe row
+        if want_out:
+            o[:, h, :] = A @ Vaff
+        for b in range(B):
+            mk = masked_rows[masked_offsets[b]:masked_offsets[b + 1]]
+            s[b] += A[mk].sum(axis=0)                                  # Eq. (5): sum over k in M_T
+    return o, lse, s
+
+
+def probe_scores(q, k_pool, v_pool, shared_slots, page_size, n_kv_heads, masked_rows,
+                 masked_offsets, scale):
+    """Eq. (5) over all layers: s_j = sum_n sum_h sum_{k in M_T} a^{(n,h)}_{j,k}.
+    q: [N][rows][Hq][d]; pools [N][n_pages][Hkv][ps][d].  Returns [B][L]."""
+    B = len(masked_offsets) - 1
+    s = np.zeros((B, len(shared_slots)))
+    for n in range(q.shape[0]):
+        _, _, sn = probe_layer(q[n], k_pool[n], v_pool[n], shared_slots, page_size, n_kv_heads,
+                               masked_rows, masked_offsets, scale, want_out=False)
+        s += sn
+    return s
+
+
+# ----------------------------------------------------------------------------
+# Top-K anchor set: Section 3.2, Eq. (6)
+# ----------------------------------------------------------------------------
+def topk_anchors(scores_b, K, affix_l):
+    """A = TopK({s_j}, K): the K affix offsets of largest score (ties to the
+    lower offset), returned as ascending logical positions l + j.
+    The non-anchor set S = F \\ A is everything else in the span."""
+    scores_b = np.asarray(scores_b)
+    order = np.lexsort((np.arange(len(scores_b)), -scores_b))   # score desc, then offset asc
+    return np.sort(order[:K]).astype(np.int64) + affix_l
+
+
+# ----------------------------------------------------------------------------
+# the two per-request maps: Section 4.1 (KV Layout and Dual Mapping) and
+# Section 4.2 (Admission-Time Preparation)
+# ----------------------------------------------------------------------------
+def build_maps(anchors_b, T, affix_l, L, shared_slots, private_pages_b, page_size):
+    """Write-side recomputation map and read-slot map of one request.
+
+    R = anchors u non-affix positions, in ascending logical order; its i-th
+    member gets private slot private_pages_b[i // ps] * ps + i % ps.
+    read_slot[p] = shared_slots[p - l] for a non-anchor affix position,
+    else the private slot of p.
+    Returns (read_slot [T], recompute_pos [R], recompute_slot [R])."""
+    anchors = set(int(a) for a in anchors_b)
+    read_slot = np.full(T, -1, np.int64)
+    rc_pos, rc_slot = [], []
+    for p in range(T):
+        in_affix = affix_l <= p < affix_l + L
+        if in_affix and p not in anchors:
+            read_slot[p] = shared_slots[p - affix_l]
+            continue
+        i = len(rc_pos)
+        slot = int(private_pages_b[i // page_size]) * page_size + i % page_size
+        rc_pos.append(p)
+        rc_slot.append(slot)
+        read_slot[p] = slot
+    return read_slot, np.array(rc_pos, np.int64), np.array(rc_slot, np.int64)
+
+
+# ----------------------------------------------------------------------------
+# write-side scatter: Section 4.3, Appendix C.1 (store-then-attend: new KV is
+# written through the write-side slot mapping first)
+# ----------------------------------------------------------------------------
+def scatter(k_pool, v_pool, k_src, v_src, dst_slots, page_size):
+    """pool[n][slot dst[i]] = src[n][i] for every layer n and KV head, one row
+    at a time.  Pools are modified in place (pass copies)."""
+    for n in range(k_src.shape[0]):
+        for i, s in enumerate(dst_slots):
+            s = int(s)
+            k_pool[n, s // page_size, :, s % page_size, :] = k_src[n, i]
+            v_pool[n, s // page_size, :, s % page_size, :] = v_src[n, i]
+
+
+# ----------------------------------------------------------------------------
+# read-slot attention: Section 4.3 (Online Inference Loop) and Appendix C.1
+# ----------------------------------------------------------------------------
+def mapped_attention_layer(q_layer, k_layer, v_layer, q_offsets, read_slot, kv_offsets,
+                           n_kv_heads, page_size, scale):
+    """Bidirectional attention of request b's query rows over every logical
+    position 0..T_b-1, whose key and value are read at physical slot
+    read_slot[kv_offsets[b] + p].
+    q_layer [n_q][Hq][d]; returns O [n_q][Hq][d] and LSE [n_q][Hq]."""
+    n_q, Hq, d = q_layer.shape
+    o = np.zeros((n_q, Hq, d))
+    lse = np.zeros((n_q, Hq))
+    for b in range(len(q_offsets) - 1):
+        q0, q1 = q_offsets[b], q_offsets[b + 1]
+        slots = read_slot[kv_offsets[b]:kv_offsets[b + 1]]
+        if q1 == q0:
+            continue
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, n_kv_heads)
+            Kl = slot_rows(k_layer, slots, g, page_size)      # [T_b][d], logical order
+            Vl = slot_rows(v_layer, slots, g, page_size)
+            Q = decode(q_layer[q0:q1, h, :])
+            A, lse[q0:q1, h] = softmax_rows((Q @ Kl.T) * scale)
+            o[q0:q1, h, :] = A @ Vl
+    return o, lse
+
+
+def block_slots(read_slot, kv_offsets, block_start, block_len):
+    """Destination slots of a decode block: request b's positions
+    block_start[b] .. +block_len, read through its read-slot map (Section 4.3,
+    Block decoding: the block's KV goes to the slots the map names)."""
+    out = []
+    for b in range(len(kv_offsets) - 1):
+        for i in range(block_len):
+            out.append(int(read_slot[kv_offsets[b] + block_start[b] + i]))
+    return np.array(out, np.int64)
