@@ -1,0 +1,241 @@
+"""ctypes binding of libacache.so (the C ABI in include/acache.h).
+
+Argument marshalling only: each function checks tensor placement, dtype and
+contiguity, turns tensors into device pointers and calls the C entry point of
+the same name on torch's current HIP stream.  Every step of the path runs in
+the library's HIP kernels; nothing here computes.  If the library is missing
+the import fails: there is no fallback.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libacache.so")
+
+ACACHE_F32, ACACHE_BF16 = 0, 1
+_DT = {torch.float32: ACACHE_F32, torch.bfloat16: ACACHE_BF16}
+
+STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ESHAPE", -4: "ERANGE", -5: "EREGION", -6: "EDUP",
+          -7: "EWORKSPACE", -8: "EDEVICE", -9: "EALIGN"}
+
+
+class AcacheError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({_lib().acache_status_string(status).decode()})")
+
+
+class KVPool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class MapArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("affix_l", ctypes.c_int32), ("L", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("seq_len", ctypes.c_void_p), ("shared_slots", ctypes.c_void_p), ("private_pages", ctypes.c_void_p),
+                ("private_page_offsets", ctypes.c_void_p), ("kv_offsets", ctypes.c_void_p),
+                ("rc_offsets", ctypes.c_void_p), ("read_slot", ctypes.c_void_p), ("recompute_pos", ctypes.c_void_p),
+                ("recompute_slot", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIG = {
+    "acache_version": ([], ctypes.c_int),
+    "acache_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "acache_anchor_count": ([_I, ctypes.c_double, ctypes.POINTER(_I)], ctypes.c_int),
+    "acache_probe_workspace_bytes": ([_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_probe_scores": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, ctypes.c_float,
+                             _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_topk_anchors": ([_P, _I, _I, _I, _I, _P, ctypes.POINTER(MapArgs), _P], ctypes.c_int),
+    "acache_build_maps": ([_P, ctypes.POINTER(MapArgs), _P], ctypes.c_int),
+    "acache_scatter_private": ([ctypes.POINTER(KVPool), _P, _P, _P, _I, _I, _I, _P], ctypes.c_int),
+    "acache_block_slots": ([_P, _P, _P, _I, _I, _P, _P], ctypes.c_int),
+    "acache_mapped_attention_workspace_bytes": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_mapped_attention": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
+                                 _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_validate_slots": ([_P, _I, _P, _P, _I, _I, _I, ctypes.POINTER(_I)], ctypes.c_int),
+}
+EXPORTS = tuple(_SIG)
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIG.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = lib
+    return _LIB
+
+
+def _check(fn, st):
+    if st != 0:
+        raise AcacheError(fn, st)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _dev(t, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return _ptr(t)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_pool(k, v, page_size=None):
+    """KVPool over tensors k, v of shape [n_layers][n_pages][n_kv_heads][page_size][head_dim]."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 5:
+        raise ValueError("k and v must be [n_layers][n_pages][n_kv_heads][page_size][head_dim] of one dtype")
+    if k.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {k.dtype}")
+    N, npg, hkv, ps, d = k.shape
+    if page_size is not None and page_size != ps:
+        raise ValueError("page_size disagrees with the pool shape")
+    return KVPool(_dev(k), _dev(v), _DT[k.dtype], N, npg, ps, hkv, d)
+
+
+def acache_version():
+    return _lib().acache_version()
+
+
+def acache_anchor_count(L, rate):
+    k = _I()
+    _check("acache_anchor_count", _lib().acache_anchor_count(int(L), float(rate), ctypes.byref(k)))
+    return k.value
+
+
+def acache_probe_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, lse_given):
+    out = ctypes.c_size_t()
+    _check("acache_probe_workspace_bytes",
+           _lib().acache_probe_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, int(bool(lse_given)),
+                                               ctypes.byref(out)))
+    return out.value
+
+
+def acache_probe_scores(pool_k, pool_v, q, masked_rows, masked_offsets, shared_slots, scores, *, max_masked,
+                        o_aff=None, lse_aff=None, layer_begin=0, scale=None, workspace=None, stream=None):
+    """Probe (Eq. 4-5).  q: [n_layers][n_rows][Hq][d]; scores [B][L] fp32 is accumulated.
+    The number of layers processed is q.shape[0], starting at pool layer `layer_begin`."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_rows, hq, d = q.shape
+    B, L = scores.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = acache_probe_workspace_bytes(n_rows, B, L, hq, n_layers, lse_aff is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _lib().acache_probe_scores(
+        ctypes.byref(pool), _dev(q, pool_k.dtype), n_rows, _dev(masked_rows, torch.int32),
+        _dev(masked_offsets, torch.int32), masked_rows.numel(), int(max_masked), _dev(shared_slots, torch.int32), L, B,
+        hq, layer_begin, n_layers, float(scale), _dev(scores, torch.float32), _dev(o_aff, pool_k.dtype),
+        _dev(lse_aff, torch.float32), _dev(workspace), workspace.numel(), _stream(stream))
+    _check("acache_probe_scores", st)
+
+
+def map_args(B, affix_l, L, K, page_size, max_seq_len, seq_len, shared_slots, private_pages, private_page_offsets,
+             kv_offsets, rc_offsets, read_slot, recompute_pos=None, recompute_slot=None):
+    i32 = torch.int32
+    return MapArgs(B, affix_l, L, K, page_size, max_seq_len, _dev(seq_len, i32), _dev(shared_slots, i32),
+                   _dev(private_pages, i32), _dev(private_page_offsets, i32), _dev(kv_offsets, i32),
+                   _dev(rc_offsets, i32), _dev(read_slot, i32), _dev(recompute_pos, i32), _dev(recompute_slot, i32))
+
+
+def acache_topk_anchors(scores, K, affix_l, anchors, maps=None, stream=None):
+    """Top-K (Eq. 6) of scores [B][L] into anchors [B][K] (ascending positions);
+    `maps` (a MapArgs) also builds the two maps."""
+    B, L = scores.shape
+    st = _lib().acache_topk_anchors(_dev(scores, torch.float32), B, L, int(K), int(affix_l),
+                                    _dev(anchors, torch.int32), ctypes.byref(maps) if maps is not None else None,
+                                    _stream(stream))
+    _check("acache_topk_anchors", st)
+
+
+def acache_build_maps(anchors, maps, stream=None):
+    _check("acache_build_maps", _lib().acache_build_maps(_dev(anchors, torch.int32), ctypes.byref(maps),
+                                                         _stream(stream)))
+
+
+def acache_scatter_private(pool_k, pool_v, k_src, v_src, dst_slots, layer_begin=0, stream=None):
+    """pool[layer_begin+n][dst_slots[i]] = src[n][i] for all KV heads.  src: [n_layers][n_rows][Hkv][d]."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_rows = k_src.shape[0], k_src.shape[1]
+    st = _lib().acache_scatter_private(ctypes.byref(pool), _dev(k_src, pool_k.dtype), _dev(v_src, pool_k.dtype),
+                                       _dev(dst_slots, torch.int32), n_rows, layer_begin, n_layers, _stream(stream))
+    _check("acache_scatter_private", st)
+
+
+def acache_block_slots(read_slot, kv_offsets, block_start, block_len, dst_slots, stream=None):
+    B = block_start.numel()
+    st = _lib().acache_block_slots(_dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32),
+                                   _dev(block_start, torch.int32), B, int(block_len), _dev(dst_slots, torch.int32),
+                                   _stream(stream))
+    _check("acache_block_slots", st)
+
+
+def acache_mapped_attention(pool_k, pool_v, q, q_offsets, read_slot, kv_offsets, out, *, max_q_per_req,
+                            max_kv_per_req, lse=None, layer_begin=0, scale=None, workspace=None, stream=None):
+    """Read-slot attention.  q/out: [n_layers][n_q][Hq][d]."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_q, hq, d = q.shape
+    B = q_offsets.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = ctypes.c_size_t()
+    _check("acache_mapped_attention_workspace_bytes",
+           _lib().acache_mapped_attention_workspace_bytes(B, n_q, hq, n_layers, ctypes.byref(ws_bytes)))
+    if workspace is None and ws_bytes.value > 0:
+        workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
+    st = _lib().acache_mapped_attention(
+        ctypes.byref(pool), _dev(q, pool_k.dtype), _dev(q_offsets, torch.int32), n_q, int(max_q_per_req),
+        _dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32), int(max_kv_per_req), B, hq, layer_begin,
+        n_layers, float(scale), _dev(out, pool_k.dtype), _dev(lse, torch.float32),
+        _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
+        _stream(stream))
+    _check("acache_mapped_attention", st)
+
+
+def acache_validate_slots(slots, page_owner, n_pages, page_size, owner=None, distinct=True):
+    """Host-side table check; slots/owner/page_owner are CPU int32 tensors or
+    numpy arrays.  Returns (status, bad_index)."""
+    import numpy as np
+
+    def host(a):
+        if a is None:
+            return None, None
+        arr = np.ascontiguousarray(a.cpu().numpy() if hasattr(a, "cpu") else a, dtype=np.int32)
+        return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+    s, sp = host(slots)
+    o, op = host(owner)
+    po, pop = host(page_owner)
+    bad = _I(-1)
+    st = _lib().acache_validate_slots(sp, len(s), op, pop, int(n_pages), int(page_size), int(bool(distinct)),
+                                      ctypes.byref(bad))
+    return st, bad.value

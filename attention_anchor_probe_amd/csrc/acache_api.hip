@@ -1,0 +1,322 @@
+// C ABI of the ACache engine: argument validation, workspace sizing and
+// kernel dispatch.  Declarations and semantics: include/acache.h.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "acache_dev.h"
+#include "acache_launch.h"
+
+using namespace acache;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == ACACHE_F32 ? 4 : 2; }
+
+int check_pool(const acache_kv_pool* p) {
+  if (!p || !p->k || !p->v) return ACACHE_EINVAL;
+  if (p->dtype != ACACHE_F32 && p->dtype != ACACHE_BF16) return ACACHE_EDTYPE;
+  if (p->n_layers <= 0 || p->n_pages <= 0 || p->n_kv_heads <= 0) return ACACHE_ESHAPE;
+  const int hd = p->head_dim;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return ACACHE_ESHAPE;
+  const int ps = p->page_size;
+  if (ps <= 0 || ps > 256 || (ps & (ps - 1))) return ACACHE_ESHAPE;
+  if ((int64_t)p->n_pages * ps > INT32_MAX) return ACACHE_ESHAPE;
+  if (!aligned16(p->k) || !aligned16(p->v)) return ACACHE_EALIGN;
+  return ACACHE_OK;
+}
+
+int check_layers(const acache_kv_pool* p, int layer_begin, int n_layers) {
+  if (layer_begin < 0 || n_layers < 0 || (int64_t)layer_begin + n_layers > p->n_layers) return ACACHE_EINVAL;
+  return ACACHE_OK;
+}
+
+int check_heads(const acache_kv_pool* p, int n_q_heads) {
+  if (n_q_heads <= 0 || n_q_heads % p->n_kv_heads != 0) return ACACHE_ESHAPE;
+  if (n_q_heads > 1024) return ACACHE_ESHAPE;
+  return ACACHE_OK;
+}
+
+PoolGeom geom_of(const acache_kv_pool* p) {
+  PoolGeom g;
+  g.n_pages = p->n_pages;
+  g.page_size = p->page_size;
+  int s = 0;
+  while ((1 << s) < p->page_size) ++s;
+  g.page_shift = s;
+  g.n_kv_heads = p->n_kv_heads;
+  g.head_dim = p->head_dim;
+  return g;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? ACACHE_OK : ACACHE_EDEVICE; }
+
+int check_map_args(const acache_map_args* m) {
+  if (!m) return ACACHE_EINVAL;
+  if (m->B < 0 || m->L <= 0 || m->affix_l < 0 || m->K < 0 || m->K > m->L || m->max_seq_len < 0)
+    return ACACHE_EINVAL;
+  if (m->page_size <= 0 || m->page_size > 256 || (m->page_size & (m->page_size - 1))) return ACACHE_ESHAPE;
+  if (m->B > 65535) return ACACHE_ESHAPE;
+  if (m->B > 0 && (!m->seq_len || !m->shared_slots || !m->private_pages || !m->private_page_offsets ||
+                   !m->kv_offsets || !m->rc_offsets || !m->read_slot))
+    return ACACHE_EINVAL;
+  return ACACHE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int acache_version(void) { return 100; }
+
+const char* acache_status_string(int s) {
+  switch (s) {
+    case ACACHE_OK: return "ok";
+    case ACACHE_EINVAL: return "invalid argument";
+    case ACACHE_EDTYPE: return "unsupported dtype";
+    case ACACHE_ESHAPE: return "unsupported shape";
+    case ACACHE_ERANGE: return "slot or index out of range";
+    case ACACHE_EREGION: return "slot outside the request's private region";
+    case ACACHE_EDUP: return "duplicate destination slot";
+    case ACACHE_EWORKSPACE: return "workspace missing or too small";
+    case ACACHE_EDEVICE: return "HIP launch error";
+    case ACACHE_EALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int acache_anchor_count(int32_t L, double rate, int32_t* K_out) {
+  if (!K_out || L < 0 || !(rate >= 0.0 && rate <= 1.0)) return ACACHE_EINVAL;
+  double k = ceil(rate * (double)L - 1e-9);
+  if (k < 0) k = 0;
+  if (k > L) k = L;
+  *K_out = (int32_t)k;
+  return ACACHE_OK;
+}
+
+int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n_q_heads, int32_t n_layers,
+                                 int32_t lse_given, size_t* bytes) {
+  if (!bytes || n_rows < 0 || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
+  size_t ws = 0;
+  if (!lse_given) ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
+  ws += align_up((size_t)n_layers * B * L * sizeof(float));
+  *bytes = ws;
+  return ACACHE_OK;
+}
+
+int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
+                        const int32_t* masked_offsets, int32_t n_masked, int32_t max_masked,
+                        const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
+                        int32_t layer_begin, int32_t n_layers, float scale, float* scores, void* o_aff,
+                        float* lse_aff, void* workspace, size_t workspace_bytes, acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if ((st = check_heads(pool, n_q_heads))) return st;
+  if (n_rows < 0 || B < 0 || L <= 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
+  if (B > 65535 || L > (1 << 24)) return ACACHE_ESHAPE;
+  if (!shared_slots || !scores) return ACACHE_EINVAL;
+  if (n_rows > 0 && !q) return ACACHE_EINVAL;
+  if (n_masked > 0 && (!masked_rows || !masked_offsets)) return ACACHE_EINVAL;
+  if (B > 0 && !masked_offsets) return ACACHE_EINVAL;
+  if (q && !aligned16(q)) return ACACHE_EALIGN;
+  if (o_aff && !aligned16(o_aff)) return ACACHE_EALIGN;
+  size_t need = 0;
+  acache_probe_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, lse_aff != nullptr, &need);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
+    return ACACHE_EWORKSPACE;
+  if (n_layers == 0 || B == 0) return ACACHE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* lse = lse_aff;
+  if (!lse) {
+    lse = (float*)ws;
+    ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
+  }
+  float* partial = (float*)ws;
+  const PoolGeom geo = geom_of(pool);
+
+  AttnArgs a;
+  a.q = q;
+  a.pool_k = (const char*)pool->k;
+  a.pool_v = (const char*)pool->v;
+  a.geo = geo;
+  a.q_offsets = nullptr;
+  a.n_q = n_rows;
+  a.max_q = n_rows;
+  a.kv_table = shared_slots;
+  a.kv_offsets = nullptr;
+  a.n_kv = L;
+  a.max_kv = L;
+  a.B = 1;
+  a.n_q_heads = n_q_heads;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.scale = scale;
+  a.out = o_aff;
+  a.lse = lse;
+  hipError_t e;
+  if (n_rows > 0) {
+    e = mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s) : launch_attn_generic(a, pool->dtype, s);
+    if (e != hipSuccess) return ACACHE_EDEVICE;
+  }
+
+  ColmassArgs c;
+  c.q = q;
+  c.pool_k = pool->k;
+  c.geo = geo;
+  c.masked_rows = masked_rows;
+  c.masked_offsets = masked_offsets;
+  c.max_masked = max_masked;
+  c.shared_slots = shared_slots;
+  c.L = L;
+  c.n_rows = n_rows;
+  c.n_q_heads = n_q_heads;
+  c.layer_begin = layer_begin;
+  c.n_layers = n_layers;
+  c.B = B;
+  c.scale = scale;
+  c.lse = lse;
+  c.partial = partial;
+  e = mfma_supported(pool->dtype, pool->head_dim) ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
+  if (e != hipSuccess) return ACACHE_EDEVICE;
+  return status_of(launch_colmass_reduce(partial, n_layers, B, L, scores, s));
+}
+
+int acache_build_maps(const int32_t* anchors, const acache_map_args* maps, acache_stream_t stream) {
+  int st;
+  if ((st = check_map_args(maps))) return st;
+  if (maps->K > 0 && maps->B > 0 && !anchors) return ACACHE_EINVAL;
+  return status_of(launch_maps(anchors, *maps, (hipStream_t)stream));
+}
+
+int acache_topk_anchors(const float* scores, int32_t B, int32_t L, int32_t K, int32_t affix_l, int32_t* anchors,
+                        const acache_map_args* maps, acache_stream_t stream) {
+  if (B < 0 || L <= 0 || K < 0 || K > L || affix_l < 0) return ACACHE_EINVAL;
+  if (L > 32768 || B > 65535) return ACACHE_ESHAPE;
+  if (B > 0 && (!scores || (K > 0 && !anchors))) return ACACHE_EINVAL;
+  if (maps) {
+    int st;
+    if ((st = check_map_args(maps))) return st;
+    if (maps->B != B || maps->L != L || maps->K != K || maps->affix_l != affix_l) return ACACHE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_topk(scores, B, L, K, affix_l, anchors, s);
+  if (e != hipSuccess) return ACACHE_EDEVICE;
+  if (maps) return status_of(launch_maps(anchors, *maps, s));
+  return ACACHE_OK;
+}
+
+int acache_scatter_private(const acache_kv_pool* pool, const void* k_src, const void* v_src,
+                           const int32_t* dst_slots, int32_t n_rows, int32_t layer_begin, int32_t n_layers,
+                           acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if (n_rows < 0) return ACACHE_EINVAL;
+  if (n_rows == 0 || n_layers == 0) return ACACHE_OK;
+  if (!k_src || !v_src || !dst_slots) return ACACHE_EINVAL;
+  if (!aligned16(k_src) || !aligned16(v_src)) return ACACHE_EALIGN;
+  if (n_layers > 65535) return ACACHE_ESHAPE;
+  return status_of(launch_scatter(pool->k, pool->v, k_src, v_src, dst_slots, n_rows, layer_begin, n_layers,
+                                  geom_of(pool), elem_bytes(pool->dtype), (hipStream_t)stream));
+}
+
+int acache_block_slots(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* block_start, int32_t B,
+                       int32_t block_len, int32_t* dst_slots, acache_stream_t stream) {
+  if (B < 0 || block_len < 0) return ACACHE_EINVAL;
+  if ((int64_t)B * block_len > INT32_MAX) return ACACHE_ESHAPE;
+  if (B == 0 || block_len == 0) return ACACHE_OK;
+  if (!read_slot || !kv_offsets || !block_start || !dst_slots) return ACACHE_EINVAL;
+  return status_of(launch_block_slots(read_slot, kv_offsets, block_start, B, block_len, dst_slots,
+                                      (hipStream_t)stream));
+}
+
+int acache_mapped_attention_workspace_bytes(int32_t B, int32_t n_q, int32_t n_q_heads, int32_t n_layers,
+                                            size_t* bytes) {
+  if (!bytes || B < 0 || n_q < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
+  *bytes = 0;
+  return ACACHE_OK;
+}
+
+int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
+                            int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
+                            int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin,
+                            int32_t n_layers, float scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if ((st = check_heads(pool, n_q_heads))) return st;
+  if (B < 0 || n_q < 0 || max_q_per_req < 0 || max_q_per_req > n_q || max_kv_per_req < 0) return ACACHE_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
+  if (B > 65535) return ACACHE_ESHAPE;
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B == 0 || n_q == 0 || n_layers == 0) return ACACHE_OK;
+  if (!q || !q_offsets || !kv_offsets || !out) return ACACHE_EINVAL;
+  if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return ACACHE_EALIGN;
+  AttnArgs a;
+  a.q = q;
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.geo = geom_of(pool);
+  a.q_offsets = q_offsets;
+  a.n_q = n_q;
+  a.max_q = max_q_per_req;
+  a.kv_table = read_slot;
+  a.kv_offsets = kv_offsets;
+  a.n_kv = 0;
+  a.max_kv = max_kv_per_req;
+  a.B = B;
+  a.n_q_heads = n_q_heads;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s)
+                                                              : launch_attn_generic(a, pool->dtype, s);
+  return status_of(e);
+}
+
+int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner, const int32_t* page_owner,
+                          int32_t n_pages, int32_t page_size, int32_t distinct, int32_t* bad_index) {
+  if (n < 0 || n_pages <= 0 || page_size <= 0 || (page_size & (page_size - 1))) return ACACHE_EINVAL;
+  if (n > 0 && (!slots || !page_owner)) return ACACHE_EINVAL;
+  const int64_t n_slots = (int64_t)n_pages * page_size;
+  std::vector<uint8_t> seen(distinct ? (size_t)n_slots : 0, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = slots[i];
+    if (s < 0 || s >= n_slots) {
+      if (bad_index) *bad_index = i;
+      return ACACHE_ERANGE;
+    }
+    const int32_t po = page_owner[s / page_size];
+    const bool ok = owner ? (po == owner[i]) : (po >= 0);
+    if (!ok) {
+      if (bad_index) *bad_index = i;
+      return ACACHE_EREGION;
+    }
+    if (distinct) {
+      if (seen[s]) {
+        if (bad_index) *bad_index = i;
+        return ACACHE_EDUP;
+      }
+      seen[s] = 1;
+    }
+  }
+  return ACACHE_OK;
+}
+
+}  // extern "C"

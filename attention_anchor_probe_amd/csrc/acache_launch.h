@@ -1,0 +1,74 @@
+// Host-side launchers of the ACache kernels (internal to the library; the C
+// ABI in acache_api.hip validates arguments and calls these).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "acache_dev.h"
+
+namespace acache {
+
+// Attention over a slot-table key list.  With q_offsets == nullptr every
+// query row attends to the single key list kv_table[0 .. n_kv) (the probe
+// over the shared affix); otherwise request b's rows q_offsets[b] ..
+// q_offsets[b+1] attend to kv_table[kv_offsets[b] .. kv_offsets[b+1]).
+struct AttnArgs {
+  const void* q;
+  const void* pool_k;
+  const void* pool_v;
+  PoolGeom geo;
+  const int32_t* q_offsets;
+  int n_q;       // rows of q per layer
+  int max_q;     // max rows per request (grid sizing)
+  const int32_t* kv_table;
+  const int32_t* kv_offsets;
+  int n_kv;      // keys when kv_offsets == nullptr
+  int max_kv;    // max keys per request
+  int B;
+  int n_q_heads;
+  int layer_begin;
+  int n_layers;
+  float scale;
+  void* out;
+  float* lse;
+};
+
+// Column mass of the masked rows (Eq. 4 weights summed over heads and rows)
+// into partial[n][b][j].
+struct ColmassArgs {
+  const void* q;
+  const void* pool_k;
+  PoolGeom geo;
+  const int32_t* masked_rows;
+  const int32_t* masked_offsets;
+  int max_masked;
+  const int32_t* shared_slots;
+  int L;
+  int n_rows;
+  int n_q_heads;
+  int layer_begin;
+  int n_layers;
+  int B;
+  float scale;
+  const float* lse;
+  float* partial;
+};
+
+hipError_t launch_topk(const float* scores, int B, int L, int K, int affix_l, int32_t* anchors, hipStream_t st);
+hipError_t launch_maps(const int32_t* anchors, const acache_map_args& a, hipStream_t st);
+hipError_t launch_block_slots(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* block_start,
+                              int B, int block_len, int32_t* dst, hipStream_t st);
+hipError_t launch_scatter(void* pool_k, void* pool_v, const void* k_src, const void* v_src, const int32_t* dst,
+                          int n_rows, int layer_begin, int n_layers, const PoolGeom& geo, int elem_bytes,
+                          hipStream_t st);
+
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t st);
+hipError_t launch_colmass_generic(const ColmassArgs& a, int dtype, hipStream_t st);
+hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int L, float* scores, hipStream_t st);
+
+// bf16, head_dim 128, MFMA kernels (k_attn_mfma.hip)
+bool mfma_supported(int dtype, int head_dim);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
+hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st);
+
+}  // namespace acache

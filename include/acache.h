@@ -1,0 +1,245 @@
+/*
+ * acache.h -- C ABI of the ACache slot-mapped bidirectional attention engine
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Affix Cache for Diffusion Large Language Models" (ACache),
+ * arXiv 2608.26140.  A shared affix F = {l, ..., l+L-1} has its KV cache
+ * computed once and stored in a shared region.  Each request runs a one-shot
+ * probe (Section 3.2, Eqs. 4-5), keeps the K affix tokens of largest
+ * masked-to-affix attention mass as Anchor Tokens (Eq. 6), recomputes only
+ * the anchors and its own positions into private slots (Section 3.3,
+ * Section 4.1 write-side map), and attends through a per-request read-slot
+ * map that names, for every logical position, the physical slot to read
+ * (Section 4.1, Section 4.3, Appendix C.1).
+ *
+ * Conventions for every call below
+ *  - Pointers are device pointers unless marked (host).  The caller owns all
+ *    memory; the library never allocates, frees or keeps a pointer after a
+ *    call returns.  Scratch memory comes from a caller workspace whose size
+ *    the matching *_workspace_bytes query reports.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return after enqueueing.  They hold no mutable global state;
+ *    calls on different streams may run concurrently when their outputs do
+ *    not overlap.
+ *  - Return value: ACACHE_OK (0) or a negative status.  Scalar, shape,
+ *    alignment and pointer checks run on the host before anything is
+ *    enqueued, so an error return means nothing was launched.  Table
+ *    *contents* (slot ids, offsets) are trusted; acache_validate_slots checks
+ *    host copies of them.  A kernel launch failure returns ACACHE_EDEVICE.
+ *  - Element types: Q, the pool, scatter sources and attention outputs share
+ *    the pool's dtype (ACACHE_F32 or ACACHE_BF16); scores and LSE are fp32;
+ *    indices and offsets are int32.  Vector pointers must be 16-byte aligned.
+ *  - head_dim is 16, 32, 64 or 128; page_size is a power of two <= 256;
+ *    n_q_heads is a multiple of n_kv_heads and query head h reads KV head
+ *    h / (n_q_heads / n_kv_heads).
+ */
+#ifndef ACACHE_H
+#define ACACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* acache_stream_t; /* hipStream_t */
+
+enum acache_status {
+  ACACHE_OK = 0,
+  ACACHE_EINVAL = -1,     /* null pointer, bad scalar (rate, K, scale, layer range) */
+  ACACHE_EDTYPE = -2,     /* unknown dtype */
+  ACACHE_ESHAPE = -3,     /* unsupported head_dim / page_size / head grouping / size limit */
+  ACACHE_ERANGE = -4,     /* slot or index out of range (acache_validate_slots) */
+  ACACHE_EREGION = -5,    /* scatter destination outside the request's private pages */
+  ACACHE_EDUP = -6,       /* duplicate scatter destination */
+  ACACHE_EWORKSPACE = -7, /* workspace missing or too small */
+  ACACHE_EDEVICE = -8,    /* HIP launch error */
+  ACACHE_EALIGN = -9      /* pointer not 16-byte aligned */
+};
+
+enum acache_dtype { ACACHE_F32 = 0, ACACHE_BF16 = 1 };
+
+/*
+ * Paged KV pool (Section 4.1: KV lives in paged physical slots; the shared
+ * region and each request's private region are sets of pages).
+ * k, v: [n_layers][n_pages][n_kv_heads][page_size][head_dim], dtype `dtype`.
+ * Physical slot s is page s / page_size, row s % page_size.
+ */
+typedef struct acache_kv_pool {
+  void* k;
+  void* v;
+  int32_t dtype;
+  int32_t n_layers;
+  int32_t n_pages;
+  int32_t page_size;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+} acache_kv_pool;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int acache_version(void);
+
+/* Static text for a status code. */
+const char* acache_status_string(int status);
+
+/*
+ * Anchor count for an affix of L tokens at anchor ratio `rate` (Section 5,
+ * Default Settings: ratios 0 to 1; ratio 0 is direct reuse, 1 is full
+ * recomputation, Section 5.1).  K = ceil(rate * L - 1e-9), clamped to [0, L].
+ * K_out (host).  EINVAL if rate is NaN or outside [0, 1], L < 0 or K_out NULL.
+ */
+int acache_anchor_count(int32_t L, double rate, int32_t* K_out);
+
+/*
+ * One-shot anchor probe, Section 3.2, Eq. (4)-(5).
+ *
+ * Every non-affix row of the batch attends over the L affix keys held in the
+ * shared region (the affix KV is fixed past state; affix rows are not
+ * forwarded):  O_aff = softmax(q K_aff^T * scale) V_aff,
+ *               LSE_aff = logsumexp(q K_aff^T * scale)   (natural log).
+ * For the initially masked rows k of request b the Eq. (4) weights
+ * a_jk = exp(q_k . k_j * scale - LSE_aff,k) are summed over query heads,
+ * masked rows and layers into scores[b][j]  (Eq. 5; the softmax normalises
+ * over the affix keys, exactly as Eq. (4) writes it).
+ *
+ *  pool            pool; layers layer_begin .. layer_begin+n_layers-1 are read
+ *  q               [n_layers][n_rows][n_q_heads][head_dim]: probe queries of
+ *                  all non-affix rows of all requests (local layer index)
+ *  n_rows          rows in q (any order; all rows share the affix)
+ *  masked_rows     [n_masked] row indices into q of the initially masked rows,
+ *                  request b's at masked_offsets[b] .. masked_offsets[b+1]-1
+ *  masked_offsets  [B+1]
+ *  n_masked        masked_offsets[B] (host copy, sizes the launch)
+ *  max_masked      max over b of masked_offsets[b+1]-masked_offsets[b] (host)
+ *  shared_slots    [L] physical slot of affix offset j
+ *  scale           softmax scale, normally 1/sqrt(head_dim) (Eq. 4)
+ *  scores          [B][L] fp32, ACCUMULATED (+=), so per-layer-group calls sum
+ *                  to Eq. (5); the caller zeroes it once per request batch
+ *  o_aff           nullable [n_layers][n_rows][n_q_heads][head_dim]
+ *  lse_aff         nullable [n_layers][n_rows][n_q_heads] fp32
+ *  workspace       >= acache_probe_workspace_bytes(...) bytes, 256-B aligned
+ * Deterministic: the same inputs give the same bits (no atomics).
+ */
+int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n_q_heads,
+                                 int32_t n_layers, int32_t lse_given, size_t* bytes /*host*/);
+
+int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_rows,
+                        const int32_t* masked_rows, const int32_t* masked_offsets,
+                        int32_t n_masked, int32_t max_masked, const int32_t* shared_slots,
+                        int32_t L, int32_t B, int32_t n_q_heads, int32_t layer_begin,
+                        int32_t n_layers, float scale, float* scores, void* o_aff,
+                        float* lse_aff, void* workspace, size_t workspace_bytes,
+                        acache_stream_t stream);
+
+/*
+ * Arguments of the per-request maps (Section 4.1 dual mapping, Section 4.2
+ * admission-time preparation).  All requests share the affix span
+ * F = {affix_l .. affix_l+L-1} and its shared slots.
+ *
+ * For request b with logical length T_b = seq_len[b] and anchors A_b, the
+ * recompute set R_b = A_b u ([0, T_b) \ F) is taken in ascending logical
+ * order; its i-th member receives private slot
+ *     private_pages[private_page_offsets[b] + i / page_size] * page_size + i % page_size.
+ * Outputs:
+ *   read_slot[kv_offsets[b] + p]  = shared_slots[p - affix_l] for p in F \ A_b,
+ *                                   else the private slot of p;
+ *   recompute_pos[rc_offsets[b] + i]  = i-th member of R_b (logical position);
+ *   recompute_slot[rc_offsets[b] + i] = its private slot (the write-side map).
+ * kv_offsets[b+1]-kv_offsets[b] must equal T_b and rc_offsets[b+1]-rc_offsets[b]
+ * must equal K + T_b - L; request b needs ceil((K + T_b - L)/page_size) pages.
+ */
+typedef struct acache_map_args {
+  int32_t B;
+  int32_t affix_l;
+  int32_t L;
+  int32_t K;
+  int32_t page_size;
+  int32_t max_seq_len;               /* host: max T_b, sizes the launch */
+  const int32_t* seq_len;            /* [B] */
+  const int32_t* shared_slots;       /* [L] */
+  const int32_t* private_pages;      /* flat page list */
+  const int32_t* private_page_offsets; /* [B+1] */
+  const int32_t* kv_offsets;         /* [B+1] */
+  const int32_t* rc_offsets;         /* [B+1] */
+  int32_t* read_slot;                /* out [kv_offsets[B]] */
+  int32_t* recompute_pos;            /* out [rc_offsets[B]], nullable */
+  int32_t* recompute_slot;           /* out [rc_offsets[B]], nullable */
+} acache_map_args;
+
+/*
+ * Anchor set, Section 3.2, Eq. (6): A_b = TopK({scores[b][j]}, K), S = F \ A_b.
+ * Exact radix select on the fp32 bit patterns: larger score first, equal
+ * scores go to the lower offset j, NaN ranks below every number, -0 equals +0.
+ * anchors [B][K] receives affix_l + j in ascending order.
+ * L <= 32768.  If `maps` is not NULL the maps are then built from these
+ * anchors on the same stream (maps->K, L, affix_l, B must agree).
+ */
+int acache_topk_anchors(const float* scores, int32_t B, int32_t L, int32_t K,
+                        int32_t affix_l, int32_t* anchors, const acache_map_args* maps,
+                        acache_stream_t stream);
+
+/* Build the two maps from given anchors ([B][K], ascending, inside F). */
+int acache_build_maps(const int32_t* anchors, const acache_map_args* maps,
+                      acache_stream_t stream);
+
+/*
+ * Write-side scatter of recomputed K/V, Section 4.3 and Appendix C.1 (store
+ * before attend).  For every local layer n, row i and KV head g:
+ *   pool.k[layer_begin+n][slot dst_slots[i]][g][:] = k_src[n][i][g][:]  (same for v)
+ * k_src, v_src: [n_layers][n_rows][n_kv_heads][head_dim], pool dtype.  A
+ * bit-exact copy.  Destinations must be distinct private slots (checked on the
+ * host by acache_validate_slots; duplicates would race).  n_rows = 0 is a no-op.
+ */
+int acache_scatter_private(const acache_kv_pool* pool, const void* k_src, const void* v_src,
+                           const int32_t* dst_slots, int32_t n_rows, int32_t layer_begin,
+                           int32_t n_layers, acache_stream_t stream);
+
+/*
+ * Destination slots of a decode block (Section 4.3, block decoding: the
+ * block's KV goes to the private slots its positions read from):
+ *   dst_slots[b*block_len + i] = read_slot[kv_offsets[b] + block_start[b] + i].
+ */
+int acache_block_slots(const int32_t* read_slot, const int32_t* kv_offsets,
+                       const int32_t* block_start, int32_t B, int32_t block_len,
+                       int32_t* dst_slots, acache_stream_t stream);
+
+/*
+ * Read-slot attention, Section 4.3 and Appendix C.1.  For request b, each of
+ * its query rows r in q_offsets[b] .. q_offsets[b+1]-1 and query head h:
+ *   O[r][h] = sum_{p < T_b} softmax_p(q[r][h] . K[s_p] * scale) V[s_p],
+ *   s_p = read_slot[kv_offsets[b] + p], K/V of KV head h / (n_q_heads/n_kv_heads).
+ * Bidirectional (no mask), ragged queries and keys, every logical position
+ * read exactly once in logical order.
+ *  q    [n_layers][n_q][n_q_heads][head_dim]; out the same shape (pool dtype);
+ *  lse  nullable [n_layers][n_q][n_q_heads] fp32 (natural log).
+ *  max_q_per_req, max_kv_per_req: host maxima that size the launch.
+ * A request with T_b = 0 gets O = 0 and LSE = -inf.
+ */
+int acache_mapped_attention_workspace_bytes(int32_t B, int32_t n_q, int32_t n_q_heads,
+                                            int32_t n_layers, size_t* bytes /*host*/);
+
+int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets,
+                            int32_t n_q, int32_t max_q_per_req, const int32_t* read_slot,
+                            const int32_t* kv_offsets, int32_t max_kv_per_req, int32_t B,
+                            int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            acache_stream_t stream);
+
+/*
+ * Host-side check of slot tables (all pointers host).  page_owner[p] is -1
+ * for a shared page, b for a page private to request b, -2 for a free page.
+ * Checks every slots[i] is in [0, n_pages*page_size) (ERANGE), lies in a page
+ * private to owner[i] (or to any request when owner is NULL) (EREGION), and,
+ * when `distinct` is non-zero, that no slot repeats (EDUP).
+ * bad_index (host, nullable) receives the first offending i.
+ */
+int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner,
+                          const int32_t* page_owner, int32_t n_pages, int32_t page_size,
+                          int32_t distinct, int32_t* bad_index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ACACHE_H */

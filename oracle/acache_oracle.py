@@ -196,7 +196,9 @@ def mapped_attention_layer(q_layer, k_layer, v_layer, q_offsets, read_slot, kv_o
     """Bidirectional attention of request b's query rows over every logical
     position 0..T_b-1, whose key and value are read at physical slot
     read_slot[kv_offsets[b] + p].
-    q_layer [n_q][Hq][d]; returns O [n_q][Hq][d] and LSE [n_q][Hq]."""
+    q_layer [n_q][Hq][d]; returns O [n_q][Hq][d] and LSE [n_q][Hq].
+    A request with no logical positions (T_b = 0) attends over an empty set:
+    its weighted sum is empty (O = 0) and its log-sum-exp is log 0 = -inf."""
     n_q, Hq, d = q_layer.shape
     o = np.zeros((n_q, Hq, d))
     lse = np.zeros((n_q, Hq))
@@ -204,6 +206,9 @@ def mapped_attention_layer(q_layer, k_layer, v_layer, q_offsets, read_slot, kv_o
         q0, q1 = q_offsets[b], q_offsets[b + 1]
         slots = read_slot[kv_offsets[b]:kv_offsets[b + 1]]
         if q1 == q0:
+            continue
+        if len(slots) == 0:
+            lse[q0:q1, :] = -np.inf
             continue
         for h in range(Hq):
             g = kv_head_of(h, Hq, n_kv_heads)

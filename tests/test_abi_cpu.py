@@ -1,0 +1,160 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before launching
+anything (so these calls never reach a HIP runtime call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_anchor_probe_amd as A
+from attention_anchor_probe_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "acache.h")
+
+FAKE = 0x10000          # 16-byte aligned non-null address: never dereferenced on these paths
+FAKE_MIS = 0x10004      # misaligned
+
+
+def declared():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(acache_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(Bd.LIB_PATH)
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Bd.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert A.acache_version() >= 100
+    lib = Bd._lib()
+    for code in range(0, -10, -1):
+        assert lib.acache_status_string(code) != b"unknown status"
+    assert lib.acache_status_string(-99) == b"unknown status"
+
+
+def test_anchor_count_matches_ceil_reading():
+    assert A.acache_anchor_count(64, 0.2) == 13
+    assert A.acache_anchor_count(1024, 0.2) == 205
+    assert A.acache_anchor_count(4096, 0.2) == 820
+    assert A.acache_anchor_count(16384, 0.3) == 4916
+    assert A.acache_anchor_count(30, 0.1) == 3
+    assert A.acache_anchor_count(5, 0.0) == 0 and A.acache_anchor_count(5, 1.0) == 5
+    for bad in (-0.1, 1.01, float("nan")):
+        with pytest.raises(A.AcacheError):
+            A.acache_anchor_count(10, bad)
+
+
+def pool(**kw):
+    base = dict(k=FAKE, v=FAKE, dtype=1, n_layers=2, n_pages=8, page_size=16, n_kv_heads=2, head_dim=128)
+    base.update(kw)
+    return Bd.KVPool(**base)
+
+
+def probe(p, **kw):
+    a = dict(q=FAKE, n_rows=10, masked_rows=FAKE, masked_offsets=FAKE, n_masked=4, max_masked=4, shared_slots=FAKE,
+             L=32, B=1, n_q_heads=4, layer_begin=0, n_layers=2, scale=0.088, scores=FAKE, o_aff=None, lse_aff=None,
+             ws=FAKE * 16, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return Bd._lib().acache_probe_scores(ctypes.byref(p), a["q"], a["n_rows"], a["masked_rows"], a["masked_offsets"],
+                                         a["n_masked"], a["max_masked"], a["shared_slots"], a["L"], a["B"],
+                                         a["n_q_heads"], a["layer_begin"], a["n_layers"], a["scale"], a["scores"],
+                                         a["o_aff"], a["lse_aff"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), None),
+    (dict(k=None), -1), (dict(dtype=5), -2), (dict(head_dim=96), -3), (dict(page_size=12), -3),
+    (dict(page_size=512), -3), (dict(n_kv_heads=0), -3), (dict(k=FAKE_MIS), -9),
+])
+def test_probe_pool_validation(kw, code):
+    st = probe(pool(**kw), B=0)    # B = 0: a valid call enqueues nothing
+    assert st == (0 if code is None else code)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=3), -3), (dict(layer_begin=1), -1), (dict(n_layers=3), -1), (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1), (dict(L=0), -1), (dict(max_masked=5), -1), (dict(shared_slots=None), -1),
+    (dict(scores=None), -1), (dict(q=FAKE_MIS), -9), (dict(ws_bytes=16), -7), (dict(ws=None), -7),
+    (dict(ws=FAKE + 16), -7),
+])
+def test_probe_argument_validation(kw, code):
+    assert probe(pool(), **kw) == code
+
+
+def test_probe_workspace_query():
+    need = A.acache_probe_workspace_bytes(100, 3, 50, 4, 2, False)
+    assert need >= 2 * 100 * 4 * 4 + 2 * 3 * 50 * 4
+    assert A.acache_probe_workspace_bytes(100, 3, 50, 4, 2, True) < need
+
+
+def test_topk_and_maps_validation():
+    lib = Bd._lib()
+    assert lib.acache_topk_anchors(FAKE, 1, 10, 11, 0, FAKE, None, None) == -1      # K > L
+    assert lib.acache_topk_anchors(FAKE, 1, 10, -1, 0, FAKE, None, None) == -1
+    assert lib.acache_topk_anchors(FAKE, 1, 40000, 5, 0, FAKE, None, None) == -3    # L above the select limit
+    assert lib.acache_topk_anchors(None, 1, 10, 5, 0, FAKE, None, None) == -1
+    m = Bd.MapArgs(1, 0, 10, 3, 16, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    m_bad = Bd.MapArgs(1, 0, 10, 4, 16, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert lib.acache_topk_anchors(FAKE, 1, 10, 3, 0, FAKE, ctypes.byref(m_bad), None) == -1   # K disagrees
+    m_ps = Bd.MapArgs(1, 0, 10, 3, 12, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert lib.acache_build_maps(FAKE, ctypes.byref(m_ps), None) == -3
+    m_null = Bd.MapArgs(1, 0, 10, 3, 16, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.acache_build_maps(FAKE, ctypes.byref(m_null), None) == -1
+    assert lib.acache_build_maps(None, ctypes.byref(m), None) == -1
+    m_empty = Bd.MapArgs(0, 0, 10, 3, 16, 0, None, None, None, None, None, None, None, None, None)
+    assert lib.acache_build_maps(None, ctypes.byref(m_empty), None) == 0
+
+
+def test_scatter_and_attention_validation():
+    lib = Bd._lib()
+    p = pool()
+    sc = lambda **kw: lib.acache_scatter_private(
+        ctypes.byref(kw.pop("pool", p)), kw.get("k", FAKE), kw.get("v", FAKE), kw.get("dst", FAKE),
+        kw.get("n", 4), kw.get("lb", 0), kw.get("nl", 2), None)
+    assert sc(n=0) == 0                     # zero rows: no-op, nothing launched
+    assert sc(nl=0) == 0
+    assert sc(n=-1) == -1
+    assert sc(k=None) == -1
+    assert sc(dst=None) == -1
+    assert sc(k=FAKE_MIS) == -9
+    assert sc(lb=1) == -1
+    assert sc(pool=pool(dtype=3)) == -2
+    at = lambda **kw: lib.acache_mapped_attention(
+        ctypes.byref(p), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE, 100,
+        kw.get("B", 1), kw.get("hq", 4), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, None, 0, None)
+    assert at(B=0) == 0
+    assert at(hq=5) == -3
+    assert at(mq=9) == -1
+    assert at(scale=-1.0) == -1
+    assert at(out=None) == -1
+    assert at(q=FAKE_MIS) == -9
+    assert lib.acache_block_slots(FAKE, FAKE, FAKE, 2, -1, FAKE, None) == -1
+    assert lib.acache_block_slots(FAKE, FAKE, FAKE, 0, 32, FAKE, None) == 0
+    assert lib.acache_block_slots(None, FAKE, FAKE, 2, 32, FAKE, None) == -1
+
+
+def test_validate_slots_host_checks():
+    ps = 4
+    owner = np.array([-1, 0, 0, 1, -2, 1], np.int32)    # page owners: shared, req0, req0, req1, free, req1
+    ok = np.array([4, 5, 9, 12, 21], np.int32)
+    assert A.acache_validate_slots(ok, owner, 6, ps) == (0, -1)
+    assert A.acache_validate_slots(np.array([4, 5, 5], np.int32), owner, 6, ps) == (-6, 2)       # EDUP
+    assert A.acache_validate_slots(np.array([4, 5, 5], np.int32), owner, 6, ps, distinct=False)[0] == 0
+    assert A.acache_validate_slots(np.array([4, 2], np.int32), owner, 6, ps) == (-5, 1)          # shared page
+    assert A.acache_validate_slots(np.array([17], np.int32), owner, 6, ps) == (-5, 0)            # free page
+    assert A.acache_validate_slots(np.array([4, 24], np.int32), owner, 6, ps) == (-4, 1)         # out of range
+    assert A.acache_validate_slots(np.array([-1], np.int32), owner, 6, ps) == (-4, 0)
+    # per-row owners: row 1 must be request 1's
+    assert A.acache_validate_slots(np.array([4, 12], np.int32), owner, 6, ps,
+                                   owner=np.array([0, 1], np.int32)) == (0, -1)
+    assert A.acache_validate_slots(np.array([4, 5], np.int32), owner, 6, ps,
+                                   owner=np.array([0, 1], np.int32)) == (-5, 1)

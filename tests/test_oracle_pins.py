@@ -494,3 +494,18 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         m.setattr(O, "topk_anchors",
                   lambda sc, kk, l: np.sort(np.lexsort((-np.arange(len(sc)), -np.asarray(sc)))[:kk]) + l)
         assert O.topk_anchors(np.array(g["scores"]), 5, g["affix_l"]).tolist() != g["cases"]["5"]
+
+
+def test_empty_context_is_empty_sum():
+    """A request with no logical positions: the attention sum is empty, so
+    O = 0 and LSE = log(0) = -inf; other requests are unaffected."""
+    w = tiny_workload()
+    K, lay, k, v, q = build_case(w)
+    qd = np_of(gen.make_rows(w, 4, gen.S_QDEC, heads=w.n_q_heads))
+    read = lay.shared_slots[:5]
+    o, lse = O.mapped_attention_layer(qd[0], k[0], v[0], [0, 2, 4], read, [0, 0, 5], w.n_kv_heads, w.page_size,
+                                      1 / math.sqrt(w.head_dim))
+    assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
+    o2, _ = O.mapped_attention_layer(qd[0][2:], k[0], v[0], [0, 2], read, [0, 5], w.n_kv_heads, w.page_size,
+                                     1 / math.sqrt(w.head_dim))
+    assert np.array_equal(o[2:], o2)
