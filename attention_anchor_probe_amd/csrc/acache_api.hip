@@ -106,7 +106,9 @@ int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n
   if (!bytes || n_rows < 0 || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
   size_t ws = 0;
   if (!lse_given) ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
-  ws += align_up((size_t)n_layers * B * L * sizeof(float));
+  // partial column masses: one per (layer, query head, request, key) on the
+  // MFMA path, one per (layer, request, key) on the vector path
+  ws += align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float));
   *bytes = ws;
   return ACACHE_OK;
 }
@@ -186,9 +188,10 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
   c.scale = scale;
   c.lse = lse;
   c.partial = partial;
-  e = mfma_supported(pool->dtype, pool->head_dim) ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
+  const bool mf = mfma_supported(pool->dtype, pool->head_dim);
+  e = mf ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
   if (e != hipSuccess) return ACACHE_EDEVICE;
-  return status_of(launch_colmass_reduce(partial, n_layers, B, L, scores, s));
+  return status_of(launch_colmass_reduce(partial, mf ? n_layers * n_q_heads : n_layers, B, L, scores, s));
 }
 
 int acache_build_maps(const int32_t* anchors, const acache_map_args* maps, acache_stream_t stream) {

@@ -1,11 +1,497 @@
-// bf16 MFMA attention kernels (gfx950), head_dim 128.
+// bf16 MFMA kernels for head_dim 128 on gfx950 (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation).
+//
+//   attn_fwd_mfma<SPLIT>  softmax(q K^T * scale) V and LSE over a key list
+//       read through a slot table: the probe forward of the non-affix rows
+//       over the shared affix (Eq. 4 of "Affix Cache for Diffusion Large
+//       Language Models", Section 3.2) and the read-slot attention of
+//       Section 4.3 / Appendix C.1.
+//       SPLIT = 0: a workgroup owns 128 query rows (32 per wave) and every
+//                  wave walks every key (many queries: probe, recompute).
+//       SPLIT = 1: a workgroup owns 32 query rows and its four waves split
+//                  each 128-key tile into four 32-key slices; the partial
+//                  (max, sum, O) of the waves are merged at the end (decode
+//                  blocks of 32 queries).
+//   colmass_mfma   the Eq. (4) weights of the masked rows recomputed as
+//       exp(q.k * scale - LSE) and summed over the rows of each request: one
+//       partial per (layer, query head, request, key); the partials are
+//       summed in a fixed order afterwards (Eq. 5), so no atomics are used.
+//
+// MFMA 32x32x16 operand mapping used throughout (lane l, g = l / 32):
+//   A (M x K): lane holds row l % 32, eight K-slots (g, j), j = 0..7
+//   B (K x N): lane holds column l % 32, the same eight K-slots
+//   C (M x N): lane holds column l % 32, rows 8*(i/4) + 4*g + i%4, i = 0..15
+// A contraction only needs A and B to agree on what each K-slot means, so
+// the head dimension is split as d = 16*c + 8*g + j for MFMA step c, and the
+// key slots of the P.V product follow the C layout of the score tile.
 #include "acache_dev.h"
 #include "acache_launch.h"
 
 namespace acache {
 
-bool mfma_supported(int dtype, int head_dim) { (void)dtype; (void)head_dim; return false; }
-hipError_t launch_attn_mfma(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_colmass_mfma(const ColmassArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int D = 128;
+constexpr int KS = D + 8;  // LDS row stride (bf16) of K and Q tiles: 272 B, spreads rows over banks
+
+struct AttnP {
+  const bf16_t* q;
+  const bf16_t* pool_k;
+  const bf16_t* pool_v;
+  PoolGeom geo;
+  const int32_t* q_offsets;
+  int n_q;
+  int q_tiles;
+  const int32_t* kv_table;
+  const int32_t* kv_offsets;
+  int n_kv;
+  int B;
+  int n_q_heads;
+  int layer_begin;
+  float c2;  // scale * log2(e)
+  bf16_t* out;
+  float* lse;
+  int n_units;
+  int per_xcd;
+};
+
+struct ColP {
+  const bf16_t* q;
+  const bf16_t* pool_k;
+  PoolGeom geo;
+  const int32_t* masked_rows;
+  const int32_t* masked_offsets;
+  const int32_t* shared_slots;
+  int L;
+  int n_rows;
+  int n_q_heads;
+  int layer_begin;
+  int B;
+  float c2;
+  const float* lse;
+  float* partial;  // [n_layers][n_q_heads][B][L]
+  int key_blocks;
+  int n_units;
+  int per_xcd;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *(const u32x4*)p; }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous run of logical units so that units sharing K/V (or Q) run on
+// the same XCD and hit its L2.
+__device__ __forceinline__ int xcd_unit(int per_xcd) {
+  const int i = blockIdx.x;
+  return (i & 7) * per_xcd + (i >> 3);
+}
+
+// Swizzle of the 8-key groups in a transposed V row (spreads the rows of one
+// column over LDS banks for both the transposing writes and the MFMA reads).
+__device__ __forceinline__ int vswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+
+// low 16 bits of the two words packed: (a & 0xffff) | (b << 16)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+}  // namespace
+
+template <int SPLIT>
+__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
+  constexpr int BN = SPLIT ? 128 : 64;   // keys per LDS tile
+  constexpr int RT = SPLIT ? 32 : 128;   // query rows per workgroup
+  constexpr int NSUB = SPLIT ? 1 : BN / 32;
+  constexpr int KLD = BN * 16 / 256;     // 16-byte K loads per thread per tile
+  constexpr int VQ = BN / 4 * 16 / 256;  // (4 keys x 8 d) V items per thread per tile
+  constexpr int KS_BYTES = BN * KS * 2;
+  constexpr int VT_BYTES = D * BN * 2;
+  constexpr int MERGE_BYTES = SPLIT ? (4 * 4 * 16 * 64 * 4 + 2 * 4 * 64 * 4) : 0;
+  constexpr int LDS_BYTES = (KS_BYTES + VT_BYTES) > MERGE_BYTES ? (KS_BYTES + VT_BYTES) : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  bf16_t* Ks = (bf16_t*)smem;
+  bf16_t* Vt = (bf16_t*)(smem + KS_BYTES);
+
+  const int unit = xcd_unit(p.per_xcd);
+  if (unit >= p.n_units) return;
+  int r = unit;
+  const int t = r % p.q_tiles;
+  r /= p.q_tiles;
+  const int b = r % p.B;
+  r /= p.B;
+  const int h = r % p.n_q_heads;
+  const int n = r / p.n_q_heads;
+  const int g = h / (p.n_q_heads / p.geo.n_kv_heads);
+  const int layer = p.layer_begin + n;
+  int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
+  if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
+  if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
+  const int rbase = q0 + t * RT;
+  if (rbase >= q1) return;
+  const int nk = k1 - k0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int qrow = SPLIT ? rbase + l32 : rbase + wave * 32 + l32;
+  const bool qvalid = qrow < q1;
+  const bool wave_live = SPLIT ? true : (rbase + wave * 32 < q1);
+
+  // Q as the B operand of S^T = K Q^T
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : q0)) * p.n_q_heads + h) * D + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+
+  u32x4 kreg[KLD], vreg[VQ * 4];
+  const int ntiles = (nk + BN - 1) / BN;
+
+  auto gload = [&](int tile) {
+    const int kb = tile * BN;
+#pragma unroll
+    for (int e = 0; e < KLD; ++e) {
+      const int u = tid + 256 * e;
+      const int key = u >> 4, dc = u & 15;
+      u32x4 x = {0, 0, 0, 0};
+      if (kb + key < nk) x = ld16(p.pool_k + p.geo.row(layer, p.kv_table[k0 + kb + key], g) + dc * 8);
+      kreg[e] = x;
+    }
+#pragma unroll
+    for (int e = 0; e < VQ; ++e) {
+      const int u = tid + 256 * e;
+      const int kq = u >> 4, dc = u & 15;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int key = kb + kq * 4 + k4;
+        u32x4 x = {0, 0, 0, 0};
+        if (key < nk) x = ld16(p.pool_v + p.geo.row(layer, p.kv_table[k0 + key], g) + dc * 8);
+        vreg[e * 4 + k4] = x;
+      }
+    }
+  };
+
+  auto lstore = [&]() {
+#pragma unroll
+    for (int e = 0; e < KLD; ++e) {
+      const int u = tid + 256 * e;
+      const int key = u >> 4, dc = u & 15;
+      *(u32x4*)(Ks + key * KS + dc * 8) = kreg[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VQ; ++e) {
+      const int u = tid + 256 * e;
+      const int kq = u >> 4, dc = u & 15;
+      const int chunk = kq >> 2, q4 = kq & 3;
+      const int grp = chunk * 2 + (q4 & 1), w0 = (q4 >> 1) * 4;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = dc * 8 + dd;
+        const int wd = dd >> 1;
+        uint32_t a0 = vreg[e * 4 + 0][wd], a1 = vreg[e * 4 + 1][wd];
+        uint32_t a2 = vreg[e * 4 + 2][wd], a3 = vreg[e * 4 + 3][wd];
+        u32x2 pk;
+        if (dd & 1) { pk[0] = pack_hi(a0, a1); pk[1] = pack_hi(a2, a3); }
+        else { pk[0] = pack_lo(a0, a1); pk[1] = pack_lo(a2, a3); }
+        *(u32x2*)(Vt + d * BN + (((grp ^ vswz(d)) << 3) | w0)) = pk;
+      }
+    }
+  };
+
+  if (ntiles > 0) gload(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (tile + 1 < ntiles) gload(tile + 1);
+    if (!wave_live) continue;
+    const int kb = tile * BN;
+    f32x16 s[NSUB];
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int sub = SPLIT ? wave : st;
+      s[st] = f32x16{};
+      const bf16_t* kp = Ks + (sub * 32 + l32) * KS + g2 * 8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[st] = mfma(as_bf16x8(*(const u32x4*)(kp + c * 16)), qf[c], s[st]);
+    }
+    // scale into the log2 domain, mask keys past the end, tile max per query
+    float mt = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int sub = SPLIT ? wave : st;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+        const float x = key < nk ? s[st][i] * p.c2 : -INFINITY;
+        s[st][i] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // rescale only when the running max grows by more than 2^8 (exact either
+    // way: O and the row sum carry the same factor)
+    if (mt > m + 8.f) {
+      const float alpha = exp2f(m - mt);
+      lsum *= alpha;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+      m = mt;
+    }
+    const float mm = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int sub = SPLIT ? wave : st;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = exp2f(s[st][8 * hh + j] - mm);
+          lsum += pv;
+          pb[j] = (__bf16)pv;
+        }
+        const int grp = sub * 4 + hh * 2 + g2;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = a * 32 + l32;
+          const bf16x8 va = as_bf16x8(*(const u32x4*)(Vt + d * BN + ((grp ^ vswz(d)) << 3)));
+          o[a] = mfma(va, pb, o[a]);
+        }
+      }
+    }
+  }
+
+  if (!SPLIT) {
+    if (!qvalid) return;
+    const float lt = lsum + __shfl_xor(lsum, 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (p.out) {
+      bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = a * 32 + 8 * i4 + 4 * g2;
+          u32x2 w;
+          w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
+          w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
+          *(u32x2*)(op + d) = w;
+        }
+    }
+    if (p.lse && g2 == 0)
+      p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    return;
+  }
+
+  // SPLIT: merge the four waves' partial results through LDS
+  float* red = (float*)smem;                      // [wave][a][i][lane]
+  float* mw = red + 4 * 4 * 16 * 64;              // [wave][lane]
+  float* lw = mw + 4 * 64;                        // [wave][lane]
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  __syncthreads();  // every wave is done with the K/V tiles
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wave * 4 + a) * 16 + i) * 64 + lane] = o[a][i];
+  mw[wave * 64 + lane] = m;
+  lw[wave * 64 + lane] = lt;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w * 64 + lane]);
+  float f[4], Lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mwv = mw[w * 64 + lane];
+    f[w] = mwv == -INFINITY ? 0.f : exp2f(mwv - M);
+    Lt += f[w] * lw[w * 64 + lane];
+  }
+  if (!qvalid) return;
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  const int a = wave;  // each wave finishes one 32-wide slice of the head dimension
+  if (p.out) {
+    bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float v4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * i4 + k;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += red[((w * 4 + a) * 16 + i) * 64 + lane] * f[w];
+        v4[k] = acc * inv;
+      }
+      const int d = a * 32 + 8 * i4 + 4 * g2;
+      u32x2 wv;
+      wv[0] = (uint32_t)f32_to_bf16(v4[0]) | ((uint32_t)f32_to_bf16(v4[1]) << 16);
+      wv[1] = (uint32_t)f32_to_bf16(v4[2]) | ((uint32_t)f32_to_bf16(v4[3]) << 16);
+      *(u32x2*)(op + d) = wv;
+    }
+  }
+  if (p.lse && wave == 0 && g2 == 0)
+    p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+}
+
+// Column mass of the masked rows.  A workgroup owns 256 affix keys (64 per
+// wave, held as two B-operand tiles in registers) of one (layer, query head)
+// and streams every request's masked rows through LDS in tiles of 32.
+__global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * KS];
+  __shared__ float lse2[32];
+  const int unit = xcd_unit(p.per_xcd);
+  if (unit >= p.n_units) return;
+  const int kblk = unit % p.key_blocks;
+  const int r = unit / p.key_blocks;
+  const int h = r % p.n_q_heads;
+  const int n = r / p.n_q_heads;
+  const int g = h / (p.n_q_heads / p.geo.n_kv_heads);
+  const int layer = p.layer_begin + n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int kw = kblk * 256 + wave * 64;  // this wave's first key
+
+  // K as the B operand of S = Q K^T (two 32-key tiles)
+  bf16x8 kf[2][8];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int j = kw + nt * 32 + l32;
+    const bool ok = j < p.L;
+    const bf16_t* kp = p.pool_k + (ok ? p.geo.row(layer, p.shared_slots[j], g) : 0) + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kf[nt][c] = ok ? as_bf16x8(ld16(kp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+
+  for (int b = 0; b < p.B; ++b) {
+    const int m0 = p.masked_offsets[b], m1 = p.masked_offsets[b + 1];
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int r0 = m0; r0 < m1; r0 += 32) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int u = tid + 256 * e;
+        const int rr = u >> 4, dc = u & 15;
+        u32x4 x = {0, 0, 0, 0};
+        if (r0 + rr < m1) {
+          const int row = p.masked_rows[r0 + rr];
+          x = ld16(p.q + (((size_t)n * p.n_rows + row) * p.n_q_heads + h) * D + dc * 8);
+        }
+        *(u32x4*)(Qs + rr * KS + dc * 8) = x;
+      }
+      if (tid < 32) {
+        float v = INFINITY;  // rows past the end contribute exp2(-inf) = 0
+        if (r0 + tid < m1) {
+          const int row = p.masked_rows[r0 + tid];
+          v = p.lse[((size_t)n * p.n_rows + row) * p.n_q_heads + h] * kLog2e;
+        }
+        lse2[tid] = v;
+      }
+      __syncthreads();
+      bf16x8 qa[8];
+      const bf16_t* qp = Qs + l32 * KS + g2 * 8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qa[c] = as_bf16x8(*(const u32x4*)(qp + c * 16));
+      float lrow[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lrow[i] = lse2[8 * (i >> 2) + 4 * g2 + (i & 3)];
+      f32x16 s0 = {}, s1 = {};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        s0 = mfma(qa[c], kf[0][c], s0);
+        s1 = mfma(qa[c], kf[1][c], s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc0 += exp2f(s0[i] * p.c2 - lrow[i]);
+        acc1 += exp2f(s1[i] * p.c2 - lrow[i]);
+      }
+    }
+    acc0 += __shfl_xor(acc0, 32, 64);
+    acc1 += __shfl_xor(acc1, 32, 64);
+    if (g2 == 0) {
+      float* dst = p.partial + (((size_t)n * p.n_q_heads + h) * p.B + b) * p.L;
+      const int j0 = kw + l32, j1 = kw + 32 + l32;
+      if (j0 < p.L) dst[j0] = acc0;
+      if (j1 < p.L) dst[j1] = acc1;
+    }
+  }
+}
+
+bool mfma_supported(int dtype, int head_dim) { return dtype == ACACHE_BF16 && head_dim == D; }
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
+  const int B = a.q_offsets ? a.B : 1;
+  const bool split = a.max_q <= 32;
+  const int RT = split ? 32 : 128;
+  AttnP p;
+  p.q = (const bf16_t*)a.q;
+  p.pool_k = (const bf16_t*)a.pool_k;
+  p.pool_v = (const bf16_t*)a.pool_v;
+  p.geo = a.geo;
+  p.q_offsets = a.q_offsets;
+  p.n_q = a.n_q;
+  p.q_tiles = (a.max_q + RT - 1) / RT;
+  p.kv_table = a.kv_table;
+  p.kv_offsets = a.kv_offsets;
+  p.n_kv = a.n_kv;
+  p.B = B;
+  p.n_q_heads = a.n_q_heads;
+  p.layer_begin = a.layer_begin;
+  p.c2 = a.scale * kLog2e;
+  p.out = (bf16_t*)a.out;
+  p.lse = a.lse;
+  const long long units = (long long)a.n_layers * a.n_q_heads * B * p.q_tiles;
+  if (units == 0) return hipSuccess;
+  if (units > (1ll << 30)) return hipErrorInvalidValue;
+  p.n_units = (int)units;
+  p.per_xcd = (int)((units + 7) / 8);
+  dim3 grid(8 * p.per_xcd), block(256);
+  if (split) hipLaunchKernelGGL(attn_fwd_mfma<1>, grid, block, 0, st, p);
+  else hipLaunchKernelGGL(attn_fwd_mfma<0>, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st) {
+  ColP p;
+  p.q = (const bf16_t*)a.q;
+  p.pool_k = (const bf16_t*)a.pool_k;
+  p.geo = a.geo;
+  p.masked_rows = a.masked_rows;
+  p.masked_offsets = a.masked_offsets;
+  p.shared_slots = a.shared_slots;
+  p.L = a.L;
+  p.n_rows = a.n_rows;
+  p.n_q_heads = a.n_q_heads;
+  p.layer_begin = a.layer_begin;
+  p.B = a.B;
+  p.c2 = a.scale * kLog2e;
+  p.lse = a.lse;
+  p.partial = a.partial;
+  p.key_blocks = (a.L + 255) / 256;
+  const long long units = (long long)a.n_layers * a.n_q_heads * p.key_blocks;
+  if (units == 0) return hipSuccess;
+  if (units > (1ll << 30)) return hipErrorInvalidValue;
+  p.n_units = (int)units;
+  p.per_xcd = (int)((units + 7) / 8);
+  hipLaunchKernelGGL(colmass_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
 
 }  // namespace acache
