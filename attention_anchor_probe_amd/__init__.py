@@ -7,6 +7,7 @@ include/acache.h); this package only binds it.
 from .binding import (  # noqa: F401
     AcacheError, KVPool, MapArgs, EXPORTS, LIB_PATH, make_pool, map_args,
     acache_version, acache_anchor_count, acache_probe_workspace_bytes, acache_probe_scores,
+    acache_probe_attention, acache_probe_column_mass_workspace_bytes, acache_probe_column_mass,
     acache_topk_anchors, acache_build_maps, acache_scatter_private, acache_block_slots,
     acache_mapped_attention, acache_validate_slots,
 )

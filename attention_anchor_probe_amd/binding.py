@@ -52,6 +52,11 @@ _SIG = {
     "acache_probe_workspace_bytes": ([_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_probe_scores": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, ctypes.c_float,
                              _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_probe_attention": ([ctypes.POINTER(KVPool), _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P],
+                               ctypes.c_int),
+    "acache_probe_column_mass_workspace_bytes": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_probe_column_mass": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I,
+                                  ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "acache_topk_anchors": ([_P, _I, _I, _I, _I, _P, ctypes.POINTER(MapArgs), _P], ctypes.c_int),
     "acache_build_maps": ([_P, ctypes.POINTER(MapArgs), _P], ctypes.c_int),
     "acache_scatter_private": ([ctypes.POINTER(KVPool), _P, _P, _P, _I, _I, _I, _P], ctypes.c_int),
@@ -157,6 +162,46 @@ def acache_probe_scores(pool_k, pool_v, q, masked_rows, masked_offsets, shared_s
         hq, layer_begin, n_layers, float(scale), _dev(scores, torch.float32), _dev(o_aff, pool_k.dtype),
         _dev(lse_aff, torch.float32), _dev(workspace), workspace.numel(), _stream(stream))
     _check("acache_probe_scores", st)
+
+
+def acache_probe_attention(pool_k, pool_v, q, shared_slots, lse_aff, *, o_aff=None, layer_begin=0, scale=None,
+                           stream=None):
+    """Probe forward only: O_aff (nullable) and LSE_aff of every row over the affix."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_rows, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib().acache_probe_attention(ctypes.byref(pool), _dev(q, pool_k.dtype), n_rows,
+                                       _dev(shared_slots, torch.int32), shared_slots.numel(), hq, layer_begin,
+                                       n_layers, float(scale), _dev(o_aff, pool_k.dtype),
+                                       _dev(lse_aff, torch.float32), _stream(stream))
+    _check("acache_probe_attention", st)
+
+
+def acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers):
+    out = ctypes.c_size_t()
+    _check("acache_probe_column_mass_workspace_bytes",
+           _lib().acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, ctypes.byref(out)))
+    return out.value
+
+
+def acache_probe_column_mass(pool_k, pool_v, q, masked_rows, masked_offsets, shared_slots, lse_aff, scores, *,
+                             max_masked, layer_begin=0, scale=None, workspace=None, stream=None):
+    """Column mass of the masked rows added to scores [B][L] (Eq. 5); lse_aff from acache_probe_attention."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_rows, hq, d = q.shape
+    B, L = scores.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = acache_probe_column_mass_workspace_bytes(B, L, hq, n_layers)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _lib().acache_probe_column_mass(
+        ctypes.byref(pool), _dev(q, pool_k.dtype), n_rows, _dev(masked_rows, torch.int32),
+        _dev(masked_offsets, torch.int32), masked_rows.numel(), int(max_masked), _dev(shared_slots, torch.int32), L,
+        B, hq, layer_begin, n_layers, float(scale), _dev(lse_aff, torch.float32), _dev(scores, torch.float32),
+        _dev(workspace), workspace.numel(), _stream(stream))
+    _check("acache_probe_column_mass", st)
 
 
 def map_args(B, affix_l, L, K, page_size, max_seq_len, seq_len, shared_slots, private_pages, private_page_offsets,

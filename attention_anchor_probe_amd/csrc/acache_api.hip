@@ -101,56 +101,52 @@ int acache_anchor_count(int32_t L, double rate, int32_t* K_out) {
   return ACACHE_OK;
 }
 
+int acache_probe_column_mass_workspace_bytes(int32_t B, int32_t L, int32_t n_q_heads, int32_t n_layers,
+                                             size_t* bytes) {
+  if (!bytes || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
+  // partial column masses: one per (layer, query head, request, key) on the
+  // MFMA path, one per (layer, request, key) on the vector path
+  *bytes = align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float));
+  return ACACHE_OK;
+}
+
 int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n_q_heads, int32_t n_layers,
                                  int32_t lse_given, size_t* bytes) {
   if (!bytes || n_rows < 0 || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
   size_t ws = 0;
   if (!lse_given) ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
-  // partial column masses: one per (layer, query head, request, key) on the
-  // MFMA path, one per (layer, request, key) on the vector path
-  ws += align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float));
-  *bytes = ws;
+  size_t cm = 0;
+  acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, &cm);
+  *bytes = ws + cm;
   return ACACHE_OK;
 }
 
-int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
-                        const int32_t* masked_offsets, int32_t n_masked, int32_t max_masked,
-                        const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
-                        int32_t layer_begin, int32_t n_layers, float scale, float* scores, void* o_aff,
-                        float* lse_aff, void* workspace, size_t workspace_bytes, acache_stream_t stream) {
+namespace {
+
+int check_probe_common(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* shared_slots,
+                       int32_t L, int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale) {
   int st;
   if ((st = check_pool(pool))) return st;
   if ((st = check_layers(pool, layer_begin, n_layers))) return st;
   if ((st = check_heads(pool, n_q_heads))) return st;
-  if (n_rows < 0 || B < 0 || L <= 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (n_rows < 0 || L <= 0) return ACACHE_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
-  if (B > 65535 || L > (1 << 24)) return ACACHE_ESHAPE;
-  if (!shared_slots || !scores) return ACACHE_EINVAL;
+  if (L > (1 << 24)) return ACACHE_ESHAPE;
+  if (!shared_slots) return ACACHE_EINVAL;
   if (n_rows > 0 && !q) return ACACHE_EINVAL;
-  if (n_masked > 0 && (!masked_rows || !masked_offsets)) return ACACHE_EINVAL;
-  if (B > 0 && !masked_offsets) return ACACHE_EINVAL;
   if (q && !aligned16(q)) return ACACHE_EALIGN;
-  if (o_aff && !aligned16(o_aff)) return ACACHE_EALIGN;
-  size_t need = 0;
-  acache_probe_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, lse_aff != nullptr, &need);
-  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
-    return ACACHE_EWORKSPACE;
-  if (n_layers == 0 || B == 0) return ACACHE_OK;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  float* lse = lse_aff;
-  if (!lse) {
-    lse = (float*)ws;
-    ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
-  }
-  float* partial = (float*)ws;
-  const PoolGeom geo = geom_of(pool);
+  return ACACHE_OK;
+}
 
+hipError_t probe_attention_launch(const acache_kv_pool* pool, const void* q, int32_t n_rows,
+                                  const int32_t* shared_slots, int32_t L, int32_t n_q_heads, int32_t layer_begin,
+                                  int32_t n_layers, float scale, void* o_aff, float* lse, hipStream_t s) {
+  if (n_rows == 0 || n_layers == 0) return hipSuccess;
   AttnArgs a;
   a.q = q;
-  a.pool_k = (const char*)pool->k;
-  a.pool_v = (const char*)pool->v;
-  a.geo = geo;
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.geo = geom_of(pool);
   a.q_offsets = nullptr;
   a.n_q = n_rows;
   a.max_q = n_rows;
@@ -165,16 +161,19 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
   a.scale = scale;
   a.out = o_aff;
   a.lse = lse;
-  hipError_t e;
-  if (n_rows > 0) {
-    e = mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s) : launch_attn_generic(a, pool->dtype, s);
-    if (e != hipSuccess) return ACACHE_EDEVICE;
-  }
+  return mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s) : launch_attn_generic(a, pool->dtype, s);
+}
 
+hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, int32_t n_rows,
+                                    const int32_t* masked_rows, const int32_t* masked_offsets, int32_t max_masked,
+                                    const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
+                                    int32_t layer_begin, int32_t n_layers, float scale, const float* lse,
+                                    float* scores, float* partial, hipStream_t s) {
+  if (n_layers == 0 || B == 0) return hipSuccess;
   ColmassArgs c;
   c.q = q;
   c.pool_k = pool->k;
-  c.geo = geo;
+  c.geo = geom_of(pool);
   c.masked_rows = masked_rows;
   c.masked_offsets = masked_offsets;
   c.max_masked = max_masked;
@@ -189,9 +188,78 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
   c.lse = lse;
   c.partial = partial;
   const bool mf = mfma_supported(pool->dtype, pool->head_dim);
-  e = mf ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
+  hipError_t e = mf ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
+  if (e != hipSuccess) return e;
+  return launch_colmass_reduce(partial, mf ? n_layers * n_q_heads : n_layers, B, L, scores, s);
+}
+
+}  // namespace
+
+int acache_probe_attention(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* shared_slots,
+                           int32_t L, int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
+                           void* o_aff, float* lse_aff, acache_stream_t stream) {
+  int st;
+  if ((st = check_probe_common(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale)))
+    return st;
+  if (!lse_aff) return ACACHE_EINVAL;
+  if (o_aff && !aligned16(o_aff)) return ACACHE_EALIGN;
+  return status_of(probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale,
+                                          o_aff, lse_aff, (hipStream_t)stream));
+}
+
+int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
+                             const int32_t* masked_offsets, int32_t n_masked, int32_t max_masked,
+                             const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
+                             int32_t layer_begin, int32_t n_layers, float scale, const float* lse_aff,
+                             float* scores, void* workspace, size_t workspace_bytes, acache_stream_t stream) {
+  int st;
+  if ((st = check_probe_common(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale)))
+    return st;
+  if (B < 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (B > 65535) return ACACHE_ESHAPE;
+  if (!scores || !lse_aff) return ACACHE_EINVAL;
+  if (n_masked > 0 && !masked_rows) return ACACHE_EINVAL;
+  if (B > 0 && !masked_offsets) return ACACHE_EINVAL;
+  size_t need = 0;
+  acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, &need);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
+    return ACACHE_EWORKSPACE;
+  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots, L,
+                                            B, n_q_heads, layer_begin, n_layers, scale, lse_aff, scores,
+                                            (float*)workspace, (hipStream_t)stream));
+}
+
+int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
+                        const int32_t* masked_offsets, int32_t n_masked, int32_t max_masked,
+                        const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
+                        int32_t layer_begin, int32_t n_layers, float scale, float* scores, void* o_aff,
+                        float* lse_aff, void* workspace, size_t workspace_bytes, acache_stream_t stream) {
+  int st;
+  if ((st = check_probe_common(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale)))
+    return st;
+  if (B < 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (B > 65535) return ACACHE_ESHAPE;
+  if (!scores) return ACACHE_EINVAL;
+  if (n_masked > 0 && !masked_rows) return ACACHE_EINVAL;
+  if (B > 0 && !masked_offsets) return ACACHE_EINVAL;
+  if (o_aff && !aligned16(o_aff)) return ACACHE_EALIGN;
+  size_t need = 0;
+  acache_probe_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, lse_aff != nullptr, &need);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
+    return ACACHE_EWORKSPACE;
+  if (n_layers == 0 || B == 0) return ACACHE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* lse = lse_aff;
+  if (!lse) {
+    lse = (float*)ws;
+    ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
+  }
+  hipError_t e = probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale,
+                                        o_aff, lse, s);
   if (e != hipSuccess) return ACACHE_EDEVICE;
-  return status_of(launch_colmass_reduce(partial, mf ? n_layers * n_q_heads : n_layers, B, L, scores, s));
+  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots, L,
+                                            B, n_q_heads, layer_begin, n_layers, scale, lse, scores, (float*)ws, s));
 }
 
 int acache_build_maps(const int32_t* anchors, const acache_map_args* maps, acache_stream_t stream) {

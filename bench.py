@@ -1,0 +1,257 @@
+"""Benchmark of the ACache slot-mapped attention path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input
+shaped like LLaDA-8B attention with a shared prefix affix of L=4096 tokens
+(32 layers, 32 heads, head_dim 128, 16 requests, 256 request tokens and 256
+generation tokens each, anchor ratio 0.2 -> K=820):
+
+  1. probe attention     O_aff, LSE_aff of the 16*512 non-affix rows over the affix
+  2. probe column mass   Eq. (4) weights of the 16*256 masked rows summed into scores
+  3. Top-K + maps        anchors (Eq. 6), read-slot and recompute maps
+  4. admission scatter   recomputed K/V of anchors + request positions -> private slots
+  5. block store         the 32-row decode block's K/V -> its private slots
+  6. read-slot attention 16 x 32 block queries over T=4608 logical keys
+
+Inputs are generated on the GPU from fixed seeds and are resident in HBM when
+the timed region starts.  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import attention_anchor_probe_amd as A  # noqa: E402
+from synth.configs import WORKLOADS, BENCH_WORKLOAD  # noqa: E402
+from synth import gen  # noqa: E402
+
+METRIC = "mapped-attention TFLOP/s (% bf16 MFMA peak); probe ms/request at affix L=4096"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=BENCH_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps (counter calibration)")
+    return ap.parse_args()
+
+
+class Setup:
+    def __init__(self, w, dev):
+        self.w, self.dev = w, dev
+        self.K = A.acache_anchor_count(w.L, w.rate)
+        lay = self.lay = gen.make_layout(w, self.K, seed=0)
+        i32 = lambda a: gen.to_device_i32(a, dev)
+        self.k, self.v = gen.make_pool(w, lay, device=dev)
+        self.q = gen.make_probe_q(w, lay, device=dev)
+        self.n_rows = self.q.shape[1]
+        self.n_rc = int(lay.rc_offsets[-1])
+        self.src_k = gen.make_rows(w, self.n_rc, gen.S_SRC_K, device=dev)
+        self.src_v = gen.make_rows(w, self.n_rc, gen.S_SRC_V, device=dev)
+        nb = w.batch * w.block_len
+        self.qd = gen.make_rows(w, nb, gen.S_QDEC, device=dev, heads=w.n_q_heads)
+        self.blk_k = gen.make_rows(w, nb, gen.S_BLK_K, device=dev)
+        self.blk_v = gen.make_rows(w, nb, gen.S_BLK_V, device=dev)
+        self.masked_rows, self.masked_offsets = i32(lay.masked_rows), i32(lay.masked_offsets)
+        self.shared_slots = i32(lay.shared_slots)
+        self.kv_offsets = i32(lay.kv_offsets)
+        self.q_off = i32(np.arange(w.batch + 1) * w.block_len)
+        self.block_start = i32(np.full(w.batch, gen.block_positions(w, 0)[0], np.int32))
+        # outputs and workspaces
+        self.o_aff = torch.empty_like(self.q)
+        self.lse_aff = torch.empty(self.q.shape[:3], device=dev)
+        self.scores = torch.zeros((w.batch, w.L), device=dev)
+        ws = A.acache_probe_column_mass_workspace_bytes(w.batch, w.L, w.n_q_heads, w.n_layers)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.anchors = torch.empty((w.batch, self.K), dtype=torch.int32, device=dev)
+        self.read_slot = torch.empty(int(lay.kv_offsets[-1]), dtype=torch.int32, device=dev)
+        self.rc_pos = torch.empty(self.n_rc, dtype=torch.int32, device=dev)
+        self.rc_slot = torch.empty_like(self.rc_pos)
+        self._keep = [i32(x) for x in (lay.seq_len, lay.shared_slots, lay.private_pages, lay.private_page_offsets,
+                                       lay.kv_offsets, lay.rc_offsets)]
+        self.maps = A.map_args(w.batch, w.affix_l, w.L, self.K, w.page_size, w.T, *self._keep, self.read_slot,
+                               self.rc_pos, self.rc_slot)
+        self.blk_dst = torch.empty(nb, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.qd)
+        torch.cuda.synchronize()
+
+    STAGES = ("probe_attention", "probe_column_mass", "topk_maps", "admission_scatter", "block_store",
+              "mapped_attention")
+
+    def step(self, ev):
+        """One pass of the path; ev[i] is recorded after stage i (ev[0] before)."""
+        w = self.w
+        ev[0].record()
+        A.acache_probe_attention(self.k, self.v, self.q, self.shared_slots, self.lse_aff, o_aff=self.o_aff)
+        ev[1].record()
+        self.scores.zero_()
+        A.acache_probe_column_mass(self.k, self.v, self.q, self.masked_rows, self.masked_offsets, self.shared_slots,
+                                   self.lse_aff, self.scores, max_masked=w.m, workspace=self.ws)
+        ev[2].record()
+        A.acache_topk_anchors(self.scores, self.K, w.affix_l, self.anchors, self.maps)
+        ev[3].record()
+        A.acache_scatter_private(self.k, self.v, self.src_k, self.src_v, self.rc_slot)
+        ev[4].record()
+        A.acache_block_slots(self.read_slot, self.kv_offsets, self.block_start, w.block_len, self.blk_dst)
+        A.acache_scatter_private(self.k, self.v, self.blk_k, self.blk_v, self.blk_dst)
+        ev[5].record()
+        A.acache_mapped_attention(self.k, self.v, self.qd, self.q_off, self.read_slot, self.kv_offsets, self.out,
+                                  max_q_per_req=w.block_len, max_kv_per_req=w.T)
+        ev[6].record()
+
+
+def work_model(w, K):
+    """Algorithmic FLOPs and bytes of each stage (what the method must compute
+    or move; unique bytes, bf16 = 2 B)."""
+    P, L, T, d, N, Hq, Hkv, B, m = w.P, w.L, w.T, w.head_dim, w.n_layers, w.n_q_heads, w.n_kv_heads, w.batch, w.m
+    e = 2
+    kv_bytes_per_pos = N * Hkv * d * e * 2          # K and V, all layers and KV heads
+    rows = B * P
+    q_bytes = N * rows * Hq * d * e
+    probe_flops = 4.0 * rows * L * d * N * Hq        # QK^T and PV over the affix (O(N H P L))
+    probe_bytes = L * kv_bytes_per_pos + 2 * q_bytes + N * rows * Hq * 4
+    cm_flops = 2.0 * B * m * L * d * N * Hq          # recomputed q.k of the masked rows (O(N H m L))
+    R = K + P
+    scatter_bytes = 2 * B * R * kv_bytes_per_pos     # read sources, write slots
+    nb = B * w.block_len
+    mapped_flops = 4.0 * nb * T * d * N * Hq
+    mapped_bytes = L * kv_bytes_per_pos + B * R * kv_bytes_per_pos + 2 * N * nb * Hq * d * e
+    return dict(probe_flops=probe_flops, probe_bytes=probe_bytes, cm_flops=cm_flops, scatter_bytes=scatter_bytes,
+                mapped_flops=mapped_flops, mapped_bytes=mapped_bytes,
+                block_bytes=2 * nb * kv_bytes_per_pos)
+
+
+def cpu_baseline(w, S, host, budget_s=20.0):
+    """The fp64 oracle, as it stands, timed on the host's cores on a bounded
+    sample of the same workload: read-slot attention of a few requests on one
+    layer (maps built by the oracle from a seeded Top-K), and the probe of one
+    request on one layer."""
+    from oracle import acache_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    lay, K = S.lay, S.K
+    scores = gen.seeded_scores(w).numpy().astype(np.float64)
+    n_req = 4
+    anchors = [O.topk_anchors(scores[b], K, w.affix_l) for b in range(n_req)]
+    read = []
+    for b in range(n_req):
+        pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+        read.append(O.build_maps(anchors[b], w.T, w.affix_l, w.L, lay.shared_slots, pp, w.page_size)[0])
+    read = np.concatenate(read)
+    kv_off = np.arange(n_req + 1) * w.T
+    q_off = np.arange(n_req + 1) * w.block_len
+    t0 = time.perf_counter()
+    O.mapped_attention_layer(host["qd0"][:n_req * w.block_len], host["k0"], host["v0"], q_off, read, kv_off,
+                             w.n_kv_heads, w.page_size, 1 / math.sqrt(w.head_dim))
+    t_map = time.perf_counter() - t0
+    mapped_flops = 4.0 * n_req * w.block_len * w.T * w.head_dim * w.n_q_heads
+    t0 = time.perf_counter()
+    rows = np.arange(w.P)
+    mk = np.array([i for i in rows if lay.probe_pos[i] in set(w.positions("gen"))], np.int32)
+    O.probe_layer(host["q0"][:w.P], host["k0"], host["v0"], lay.shared_slots, w.page_size, w.n_kv_heads, mk,
+                  np.array([0, len(mk)]), 1 / math.sqrt(w.head_dim))
+    t_probe = time.perf_counter() - t0
+    return {"value": mapped_flops / t_map / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"read-slot attention of {n_req} requests x {w.block_len} queries x {w.n_q_heads} heads over "
+                       f"T={w.T} keys on 1 of {w.n_layers} layers ({t_map:.1f} s); probe of 1 request "
+                       f"({w.P} rows) on 1 layer ({t_probe:.1f} s)"),
+            "probe_ms_per_request_extrapolated": t_probe * w.n_layers * 1e3,
+            "seconds": t_map + t_probe}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path shards by request with no exchange, and this build "
+              "runs and reports a single GPU only (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    w = WORKLOADS[args.workload]
+    S = Setup(w, dev)
+    host = None
+    if not args.no_cpu_baseline:
+        def np_of(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        host = {"k0": np_of(S.k[0]), "v0": np_of(S.v[0]), "q0": np_of(S.q[0]), "qd0": np_of(S.qd[0])}
+    if args.calib_copy_mib:
+        x = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+    nst = len(Setup.STAGES)
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+    for _ in range(args.warmup):
+        S.step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        S.step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(Setup.STAGES)}
+    wm = work_model(w, S.K)
+    t_map = stage_ms["mapped_attention"] * 1e-3
+    t_probe = stage_ms["probe_attention"] * 1e-3
+    mapped_tflops = wm["mapped_flops"] / t_map / 1e12
+    probe_ms_req = (stage_ms["probe_attention"] + stage_ms["probe_column_mass"] + stage_ms["topk_maps"]) / w.batch
+    probe_tflops = wm["probe_flops"] / t_probe / 1e12
+    roof = {"kernel": "attn_fwd_mfma<0> (probe attention, one launch for all layers)", "bound": "mfma",
+            "achieved": probe_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+            "algorithmic_per_launch": wm["probe_flops"]}
+    mapped_gbs = wm["mapped_bytes"] / t_map / 1e9
+    roof_mapped = {"kernel": "attn_fwd_mfma<1> (read-slot attention, one launch for all layers)", "bound": "hbm",
+                   "achieved": mapped_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": mapped_gbs / PEAK_HBM_GBS,
+                   "traffic": None, "algorithmic_per_launch": wm["mapped_bytes"]}
+    scatter_gbs = wm["scatter_bytes"] / (stage_ms["admission_scatter"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": mapped_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "affix_L": w.L, "affix_at": w.affix_l, "request_tokens": w.P - w.m,
+                   "gen_tokens": w.m, "batch": w.batch, "anchor_rate": w.rate, "K": S.K, "decode_block": w.block_len,
+                   "logical_len": w.T, "page_size": w.page_size, "page_order": w.page_order},
+        "mapped_attention_pct_bf16_peak": 100.0 * mapped_tflops / PEAK_BF16_TFLOPS,
+        "probe_ms_per_request": probe_ms_req,
+        "probe_attention_tflops": probe_tflops,
+        "admission_scatter_gbs": scatter_gbs,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+        "roofline_mapped": roof_mapped,
+    }
+    if host is not None:
+        out["cpu_baseline"] = cpu_baseline(w, S, host)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

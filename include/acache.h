@@ -133,6 +133,35 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
                         acache_stream_t stream);
 
 /*
+ * The two halves of acache_probe_scores, for callers that schedule them
+ * separately (same semantics, same arguments).
+ *
+ * acache_probe_attention: O_aff and LSE_aff of every probe row over the affix
+ * (the O(N H P L) probe forward of Section 3.2).  lse_aff is required (the
+ * column mass reads it); o_aff is nullable.  No workspace.
+ *
+ * acache_probe_column_mass: the Eq. (4) weights of the masked rows,
+ * a_jk = exp(q_k . k_j * scale - LSE_aff,k), summed over query heads, masked
+ * rows and layers and ADDED to scores[b][j] (Eq. 5), in a fixed order.  Reads
+ * the lse_aff written by acache_probe_attention for the same q.  Workspace of
+ * acache_probe_column_mass_workspace_bytes(...) bytes, 256-B aligned.
+ */
+int acache_probe_attention(const acache_kv_pool* pool, const void* q, int32_t n_rows,
+                           const int32_t* shared_slots, int32_t L, int32_t n_q_heads,
+                           int32_t layer_begin, int32_t n_layers, float scale, void* o_aff,
+                           float* lse_aff, acache_stream_t stream);
+
+int acache_probe_column_mass_workspace_bytes(int32_t B, int32_t L, int32_t n_q_heads,
+                                             int32_t n_layers, size_t* bytes /*host*/);
+
+int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t n_rows,
+                             const int32_t* masked_rows, const int32_t* masked_offsets,
+                             int32_t n_masked, int32_t max_masked, const int32_t* shared_slots,
+                             int32_t L, int32_t B, int32_t n_q_heads, int32_t layer_begin,
+                             int32_t n_layers, float scale, const float* lse_aff, float* scores,
+                             void* workspace, size_t workspace_bytes, acache_stream_t stream);
+
+/*
  * Arguments of the per-request maps (Section 4.1 dual mapping, Section 4.2
  * admission-time preparation).  All requests share the affix span
  * F = {affix_l .. affix_l+L-1} and its shared slots.
