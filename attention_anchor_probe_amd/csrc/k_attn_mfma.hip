@@ -50,6 +50,7 @@ struct AttnP {
   const int32_t* kv_table;
   const int32_t* kv_offsets;
   int n_kv;
+  size_t layer_bytes;  // bytes of one layer of the K (or V) pool, < 4 GiB
   int B;
   int n_q_heads;
   int layer_begin;
@@ -159,30 +160,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
   u32x4 kreg[KLD], vreg[VQ * 4];
+  uint32_t koff[KLD], voff[VQ * 4];
   const int ntiles = (nk + BN - 1) / BN;
+  // one layer of the pool is addressed from a scalar base with 32-bit byte offsets
+  const char* kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
+  const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
+  const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * D * 2;
+  const uint32_t head_off = (uint32_t)g * p.geo.page_size * D * 2 + (uint32_t)(tid & 15) * 16;
+  auto slot_off = [&](int32_t slot) -> uint32_t {
+    return ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
+           ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * (D * 2);
+  };
 
-  auto gload = [&](int tile) {
+  // Slots of a tile are loaded one tile ahead of its K/V rows, so a row load
+  // never waits on the table load that names it.  Keys past the end are
+  // clamped to the last key (their scores are masked to -inf below, so their
+  // rows only ever meet a zero weight).
+  auto sload = [&](int tile) {
     const int kb = tile * BN;
 #pragma unroll
     for (int e = 0; e < KLD; ++e) {
-      const int u = tid + 256 * e;
-      const int key = u >> 4, dc = u & 15;
-      u32x4 x = {0, 0, 0, 0};
-      if (kb + key < nk) x = ld16(p.pool_k + p.geo.row(layer, p.kv_table[k0 + kb + key], g) + dc * 8);
-      kreg[e] = x;
+      const int key = min(kb + (tid >> 4) + 16 * e, nk - 1);
+      koff[e] = (uint32_t)p.kv_table[k0 + key];
     }
 #pragma unroll
-    for (int e = 0; e < VQ; ++e) {
-      const int u = tid + 256 * e;
-      const int kq = u >> 4, dc = u & 15;
+    for (int e = 0; e < VQ; ++e)
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        const int key = kb + kq * 4 + k4;
-        u32x4 x = {0, 0, 0, 0};
-        if (key < nk) x = ld16(p.pool_v + p.geo.row(layer, p.kv_table[k0 + key], g) + dc * 8);
-        vreg[e * 4 + k4] = x;
+        const int key = min(kb + 4 * ((tid >> 4) + 16 * e) + k4, nk - 1);
+        voff[e * 4 + k4] = (uint32_t)p.kv_table[k0 + key];
       }
-    }
+  };
+  auto dload = [&]() {
+#pragma unroll
+    for (int e = 0; e < KLD; ++e) kreg[e] = *(const u32x4*)(kbase + slot_off((int32_t)koff[e]));
+#pragma unroll
+    for (int e = 0; e < VQ * 4; ++e) vreg[e] = *(const u32x4*)(vbase + slot_off((int32_t)voff[e]));
   };
 
   auto lstore = [&]() {
@@ -212,12 +225,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
     }
   };
 
-  if (ntiles > 0) gload(0);
+  if (ntiles > 0) {
+    sload(0);
+    dload();
+    if (ntiles > 1) sload(1);
+  }
   for (int tile = 0; tile < ntiles; ++tile) {
     __syncthreads();
     lstore();
     __syncthreads();
-    if (tile + 1 < ntiles) gload(tile + 1);
+    if (tile + 1 < ntiles) {
+      dload();
+      if (tile + 2 < ntiles) sload(tile + 2);
+    }
     if (!wave_live) continue;
     const int kb = tile * BN;
     f32x16 s[NSUB];
@@ -451,6 +471,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   p.kv_table = a.kv_table;
   p.kv_offsets = a.kv_offsets;
   p.n_kv = a.n_kv;
+  p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
+  if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
   p.B = B;
   p.n_q_heads = a.n_q_heads;
   p.layer_begin = a.layer_begin;
