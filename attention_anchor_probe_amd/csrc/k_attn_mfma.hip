@@ -85,6 +85,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *(const u32x4*)p; }
 
+// 2^x on the hardware exp unit (v_exp_f32): results below 2^-126 flush
+// toward zero, which is harmless for softmax weights; exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -249,20 +253,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) s[st] = mfma(as_bf16x8(*(const u32x4*)(kp + c * 16)), qf[c], s[st]);
     }
-    // scale into the log2 domain, mask keys past the end, tile max per query
-    float mt = -INFINITY;
+    // keys past the end (tail tile only) get -inf; the running max m lives in
+    // the scaled log2 domain, c2 > 0, so max(s) * c2 is the scaled tile max
+    if (kb + BN > nk) {
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-      const int sub = SPLIT ? wave : st;
+      for (int st = 0; st < NSUB; ++st) {
+        const int sub = SPLIT ? wave : st;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
-        const float x = key < nk ? s[st][i] * p.c2 : -INFINITY;
-        s[st][i] = x;
-        mt = fmaxf(mt, x);
+        for (int i = 0; i < 16; ++i)
+          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[st][i] = -INFINITY;
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    float mr = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[st][i]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    const float mt = mr * p.c2;
     // rescale only when the running max grows by more than 2^8 (exact either
     // way: O and the row sum carry the same factor)
     if (mt > m + 8.f) {
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
         for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
       m = mt;
     }
-    const float mm = (m == -INFINITY) ? 0.f : m;
+    const float nm = (m == -INFINITY) ? 0.f : -m;
 #pragma unroll
     for (int st = 0; st < NSUB; ++st) {
       const int sub = SPLIT ? wave : st;
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pv = exp2f(s[st][8 * hh + j] - mm);
+          const float pv = fast_exp2(fmaf(s[st][8 * hh + j], p.c2, nm));
           lsum += pv;
           pb[j] = (__bf16)pv;
         }
@@ -372,10 +380,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
 
 // Column mass of the masked rows.  A workgroup owns 256 affix keys (64 per
 // wave, held as two B-operand tiles in registers) of one (layer, query head)
-// and streams every request's masked rows through LDS in tiles of 32.
+// and streams every request's masked rows through LDS in tiles of 32.  The
+// tiles of all requests are walked as one list; row indices are loaded two
+// tiles ahead and Q rows / LSE values one tile ahead of their use.
 __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * KS];
-  __shared__ float lse2[32];
+  __shared__ __attribute__((aligned(16))) float lse2[32];
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
   const int kblk = unit % p.key_blocks;
@@ -392,65 +402,99 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   bf16x8 kf[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const int j = kw + nt * 32 + l32;
-    const bool ok = j < p.L;
-    const bf16_t* kp = p.pool_k + (ok ? p.geo.row(layer, p.shared_slots[j], g) : 0) + g2 * 8;
+    const int j = min(kw + nt * 32 + l32, p.L - 1);
+    const bf16_t* kp = p.pool_k + p.geo.row(layer, p.shared_slots[j], g) + g2 * 8;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kf[nt][c] = ok ? as_bf16x8(ld16(kp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int c = 0; c < 8; ++c) kf[nt][c] = as_bf16x8(ld16(kp + c * 16));
   }
 
-  for (int b = 0; b < p.B; ++b) {
-    const int m0 = p.masked_offsets[b], m1 = p.masked_offsets[b + 1];
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int r0 = m0; r0 < m1; r0 += 32) {
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int u = tid + 256 * e;
-        const int rr = u >> 4, dc = u & 15;
-        u32x4 x = {0, 0, 0, 0};
-        if (r0 + rr < m1) {
-          const int row = p.masked_rows[r0 + rr];
-          x = ld16(p.q + (((size_t)n * p.n_rows + row) * p.n_q_heads + h) * D + dc * 8);
-        }
-        *(u32x4*)(Qs + rr * KS + dc * 8) = x;
-      }
-      if (tid < 32) {
-        float v = INFINITY;  // rows past the end contribute exp2(-inf) = 0
-        if (r0 + tid < m1) {
-          const int row = p.masked_rows[r0 + tid];
-          v = p.lse[((size_t)n * p.n_rows + row) * p.n_q_heads + h] * kLog2e;
-        }
-        lse2[tid] = v;
-      }
-      __syncthreads();
-      bf16x8 qa[8];
-      const bf16_t* qp = Qs + l32 * KS + g2 * 8;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qa[c] = as_bf16x8(*(const u32x4*)(qp + c * 16));
-      float lrow[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lrow[i] = lse2[8 * (i >> 2) + 4 * g2 + (i & 3)];
-      f32x16 s0 = {}, s1 = {};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        s0 = mfma(qa[c], kf[0][c], s0);
-        s1 = mfma(qa[c], kf[1][c], s1);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc0 += exp2f(s0[i] * p.c2 - lrow[i]);
-        acc1 += exp2f(s1[i] * p.c2 - lrow[i]);
-      }
+  float* part = p.partial + ((size_t)n * p.n_q_heads + h) * p.B * p.L;
+  const int j0 = kw + l32, j1 = kw + 32 + l32;
+  // requests without masked rows contribute zero
+  for (int b = 0; b < p.B; ++b)
+    if (p.masked_offsets[b + 1] == p.masked_offsets[b] && g2 == 0) {
+      if (j0 < p.L) part[(size_t)b * p.L + j0] = 0.f;
+      if (j1 < p.L) part[(size_t)b * p.L + j1] = 0.f;
     }
-    acc0 += __shfl_xor(acc0, 32, 64);
-    acc1 += __shfl_xor(acc1, 32, 64);
-    if (g2 == 0) {
-      float* dst = p.partial + (((size_t)n * p.n_q_heads + h) * p.B + b) * p.L;
-      const int j0 = kw + l32, j1 = kw + 32 + l32;
-      if (j0 < p.L) dst[j0] = acc0;
-      if (j1 < p.L) dst[j1] = acc1;
+
+  // tile iterator over (request, first masked row) of all non-empty requests
+  struct It { int b, r0, m1; };
+  auto first_from = [&](int b) -> It {
+    while (b < p.B && p.masked_offsets[b + 1] == p.masked_offsets[b]) ++b;
+    if (b >= p.B) return It{p.B, 0, 0};
+    return It{b, p.masked_offsets[b], p.masked_offsets[b + 1]};
+  };
+  auto next = [&](It t) -> It {
+    if (t.b >= p.B) return t;
+    if (t.r0 + 32 < t.m1) return It{t.b, t.r0 + 32, t.m1};
+    return first_from(t.b + 1);
+  };
+
+  const int rr0 = tid >> 4, rr1 = 16 + (tid >> 4), dc = tid & 15;
+  int ri0 = 0, ri1 = 0, ril = 0;        // masked-row indices of a tile
+  u32x4 q0 = {0, 0, 0, 0}, q1 = {0, 0, 0, 0};
+  float lv = INFINITY;
+  auto rows_load = [&](It t) {
+    ri0 = p.masked_rows[min(t.r0 + rr0, t.m1 - 1)];
+    ri1 = p.masked_rows[min(t.r0 + rr1, t.m1 - 1)];
+    if (tid < 32) ril = p.masked_rows[min(t.r0 + tid, t.m1 - 1)];
+  };
+  auto q_load = [&](It t) {
+    const size_t base = (size_t)n * p.n_rows;
+    q0 = ld16(p.q + ((base + ri0) * p.n_q_heads + h) * D + dc * 8);
+    q1 = ld16(p.q + ((base + ri1) * p.n_q_heads + h) * D + dc * 8);
+    if (tid < 32) lv = t.r0 + tid < t.m1 ? p.lse[(base + ril) * p.n_q_heads + h] * kLog2e : INFINITY;
+  };
+
+  It t0 = first_from(0);
+  It t1 = next(t0);
+  if (t0.b < p.B) {
+    rows_load(t0);
+    q_load(t0);
+    if (t1.b < p.B) rows_load(t1);
+  }
+  float acc0 = 0.f, acc1 = 0.f;
+  while (t0.b < p.B) {
+    const It t2 = next(t1);
+    __syncthreads();
+    // rows past the request's end carry LSE = +inf, so they add exp2(-inf) = 0
+    *(u32x4*)(Qs + rr0 * KS + dc * 8) = q0;
+    *(u32x4*)(Qs + rr1 * KS + dc * 8) = q1;
+    if (tid < 32) lse2[tid] = lv;
+    __syncthreads();
+    if (t1.b < p.B) {
+      q_load(t1);
+      if (t2.b < p.B) rows_load(t2);
     }
+    bf16x8 qa[8];
+    const bf16_t* qp = Qs + l32 * KS + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qa[c] = as_bf16x8(*(const u32x4*)(qp + c * 16));
+    float lrow[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lrow[i] = lse2[8 * (i >> 2) + 4 * g2 + (i & 3)];
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s0 = mfma(qa[c], kf[0][c], s0);
+      s1 = mfma(qa[c], kf[1][c], s1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc0 += fast_exp2(fmaf(s0[i], p.c2, -lrow[i]));
+      acc1 += fast_exp2(fmaf(s1[i], p.c2, -lrow[i]));
+    }
+    if (t1.b != t0.b) {  // last tile of this request: write its partial column masses
+      const float a0 = acc0 + __shfl_xor(acc0, 32, 64);
+      const float a1 = acc1 + __shfl_xor(acc1, 32, 64);
+      if (g2 == 0) {
+        if (j0 < p.L) part[(size_t)t0.b * p.L + j0] = a0;
+        if (j1 < p.L) part[(size_t)t0.b * p.L + j1] = a1;
+      }
+      acc0 = acc1 = 0.f;
+    }
+    t0 = t1;
+    t1 = t2;
   }
 }
 
