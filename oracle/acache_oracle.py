@@ -63,14 +63,11 @@ def anchor_count(L, rate):
 # offset s % ps)
 # ----------------------------------------------------------------------------
 def slot_rows(pool_layer, slots, kv_head, page_size):
-    """Gather one KV head's rows for a list of physical slots, one slot at a
-    time.  pool_layer: [n_pages][Hkv][page_size][d] (stored values)."""
-    d = pool_layer.shape[-1]
-    out = np.empty((len(slots), d), np.float64)
-    for i, s in enumerate(slots):
-        s = int(s)
-        out[i] = decode(pool_layer[s // page_size, kv_head, s % page_size])
-    return out
+    """Gather one KV head's rows for a list of physical slots: row i is
+    pool_layer[page(slots[i]), kv_head, offset(slots[i])], in the order of
+    `slots`.  pool_layer: [n_pages][Hkv][page_size][d] (stored values)."""
+    slots = np.asarray(slots, np.int64)
+    return decode(pool_layer[slots // page_size, kv_head, slots % page_size])
 
 
 def kv_head_of(h, n_q_heads, n_kv_heads):
@@ -110,11 +107,10 @@ def probe_layer(q_layer, k_layer, v_layer, shared_slots, page_size, n_kv_heads,
     for h in range(Hq):
         g = kv_head_of(h, Hq, n_kv_heads)
         Kaff = slot_rows(k_layer, shared_slots, g, page_size)      # [L][d]
-        Vaff = slot_rows(v_layer, shared_slots, g, page_size)
         Q = decode(q_layer[:, h, :])                                  # [rows][d]
         A, lse[:, h] = softmax_rows((Q @ Kaff.T) * scale)             # Eq. (4), every probe row
         if want_out:
-            o[:, h, :] = A @ Vaff
+            o[:, h, :] = A @ slot_rows(v_layer, shared_slots, g, page_size)
         for b in range(B):
             mk = masked_rows[masked_offsets[b]:masked_offsets[b + 1]]
             s[b] += A[mk].sum(axis=0)                                  # Eq. (5): sum over k in M_T
