@@ -135,11 +135,27 @@ def work_model(w, K):
                 block_bytes=2 * nb * kv_bytes_per_pos)
 
 
-def cpu_baseline(w, S, host, budget_s=20.0):
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the counters' reading of a 1 GiB device copy), or None for
+    a kernel whose source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "attention_anchor_probe_amd", "csrc", "k_attn_mfma.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"].get("k_attn_mfma.hip"):
+        return {}
+    return {k: v["hbm_bytes"] for k, v in rec["kernels"].items()}
+
+
+def cpu_baseline(w, S, host, target_s=10.0):
     """The fp64 oracle, as it stands, timed on the host's cores on a bounded
-    sample of the same workload: read-slot attention of a few requests on one
-    layer (maps built by the oracle from a seeded Top-K), and the probe of one
-    request on one layer."""
+    sample of the same workload, grown layer by layer until each part has run
+    for about target_s seconds: read-slot attention of all requests' decode
+    blocks (maps built by the oracle from a seeded Top-K), and the probe of all
+    requests' rows (extrapolated to all layers for ms/request)."""
     from oracle import acache_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -147,32 +163,41 @@ def cpu_baseline(w, S, host, budget_s=20.0):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     lay, K = S.lay, S.K
+    scale = 1 / math.sqrt(w.head_dim)
     scores = gen.seeded_scores(w).numpy().astype(np.float64)
-    n_req = 4
-    anchors = [O.topk_anchors(scores[b], K, w.affix_l) for b in range(n_req)]
+    anchors = [O.topk_anchors(scores[b], K, w.affix_l) for b in range(w.batch)]
     read = []
-    for b in range(n_req):
+    for b in range(w.batch):
         pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
         read.append(O.build_maps(anchors[b], w.T, w.affix_l, w.L, lay.shared_slots, pp, w.page_size)[0])
     read = np.concatenate(read)
-    kv_off = np.arange(n_req + 1) * w.T
-    q_off = np.arange(n_req + 1) * w.block_len
-    t0 = time.perf_counter()
-    O.mapped_attention_layer(host["qd0"][:n_req * w.block_len], host["k0"], host["v0"], q_off, read, kv_off,
-                             w.n_kv_heads, w.page_size, 1 / math.sqrt(w.head_dim))
-    t_map = time.perf_counter() - t0
-    mapped_flops = 4.0 * n_req * w.block_len * w.T * w.head_dim * w.n_q_heads
-    t0 = time.perf_counter()
-    rows = np.arange(w.P)
-    mk = np.array([i for i in rows if lay.probe_pos[i] in set(w.positions("gen"))], np.int32)
-    O.probe_layer(host["q0"][:w.P], host["k0"], host["v0"], lay.shared_slots, w.page_size, w.n_kv_heads, mk,
-                  np.array([0, len(mk)]), 1 / math.sqrt(w.head_dim))
-    t_probe = time.perf_counter() - t0
+    q_off = np.arange(w.batch + 1) * w.block_len
+    t_map, n_map = 0.0, 0
+    for n in range(len(host["k"])):
+        t0 = time.perf_counter()
+        O.mapped_attention_layer(host["qd"][n], host["k"][n], host["v"][n], q_off, read, lay.kv_offsets,
+                                 w.n_kv_heads, w.page_size, scale)
+        t_map += time.perf_counter() - t0
+        n_map += 1
+        if t_map >= target_s:
+            break
+    mapped_flops = 4.0 * w.batch * w.block_len * w.T * w.head_dim * w.n_q_heads * n_map
+    t_probe, n_probe = 0.0, 0
+    for n in range(len(host["k"])):
+        t0 = time.perf_counter()
+        O.probe_layer(host["q"][n], host["k"][n], host["v"][n], lay.shared_slots, w.page_size, w.n_kv_heads,
+                      lay.masked_rows, lay.masked_offsets, scale)
+        t_probe += time.perf_counter() - t0
+        n_probe += 1
+        if t_probe >= target_s:
+            break
+    probe_ms_req = t_probe / n_probe * w.n_layers / w.batch * 1e3
     return {"value": mapped_flops / t_map / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"read-slot attention of {n_req} requests x {w.block_len} queries x {w.n_q_heads} heads over "
-                       f"T={w.T} keys on 1 of {w.n_layers} layers ({t_map:.1f} s); probe of 1 request "
-                       f"({w.P} rows) on 1 layer ({t_probe:.1f} s)"),
-            "probe_ms_per_request_extrapolated": t_probe * w.n_layers * 1e3,
+            "sample": (f"read-slot attention of all {w.batch} requests x {w.block_len} queries x {w.n_q_heads} heads "
+                       f"over T={w.T} keys on {n_map} of {w.n_layers} layers ({t_map:.1f} s); probe of all "
+                       f"{w.batch * w.P} rows on {n_probe} of {w.n_layers} layers ({t_probe:.1f} s), its ms/request "
+                       f"extrapolated to {w.n_layers} layers"),
+            "probe_ms_per_request_extrapolated": probe_ms_req,
             "seconds": t_map + t_probe}
 
 
@@ -193,7 +218,9 @@ def main():
         def np_of(t):
             t = t.detach().cpu().contiguous()
             return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
-        host = {"k0": np_of(S.k[0]), "v0": np_of(S.v[0]), "q0": np_of(S.q[0]), "qd0": np_of(S.qd[0])}
+        n_snap = min(w.n_layers, 8)
+        host = {"k": [np_of(S.k[n]) for n in range(n_snap)], "v": [np_of(S.v[n]) for n in range(n_snap)],
+                "q": [np_of(S.q[n]) for n in range(n_snap)], "qd": [np_of(S.qd[n]) for n in range(n_snap)]}
     if args.calib_copy_mib:
         x = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
@@ -223,14 +250,17 @@ def main():
     mapped_tflops = wm["mapped_flops"] / t_map / 1e12
     probe_ms_req = (stage_ms["probe_attention"] + stage_ms["probe_column_mass"] + stage_ms["topk_maps"]) / w.batch
     probe_tflops = wm["probe_flops"] / t_probe / 1e12
+    traffic = measured_traffic(w.name)
     roof = {"kernel": "attn_fwd_mfma<0> (probe attention, one launch for all layers)", "bound": "mfma",
             "achieved": probe_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-            "algorithmic_per_launch": wm["probe_flops"]}
+            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get("attn_fwd_mfma<0>"),
+            "traffic_unit": "HBM bytes per launch", "algorithmic_per_launch": wm["probe_flops"],
+            "algorithmic_bytes_per_launch": wm["probe_bytes"]}
     mapped_gbs = wm["mapped_bytes"] / t_map / 1e9
     roof_mapped = {"kernel": "attn_fwd_mfma<1> (read-slot attention, one launch for all layers)", "bound": "hbm",
                    "achieved": mapped_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": mapped_gbs / PEAK_HBM_GBS,
-                   "traffic": None, "algorithmic_per_launch": wm["mapped_bytes"]}
+                   "traffic": traffic.get("attn_fwd_mfma<1>"), "traffic_unit": "HBM bytes per launch",
+                   "algorithmic_per_launch": wm["mapped_bytes"]}
     scatter_gbs = wm["scatter_bytes"] / (stage_ms["admission_scatter"] * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": mapped_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
