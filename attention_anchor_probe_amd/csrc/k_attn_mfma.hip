@@ -1,17 +1,16 @@
 // bf16 MFMA kernels for head_dim 128 on gfx950 (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation).
 //
-//   attn_fwd_mfma<SPLIT>  softmax(q K^T * scale) V and LSE over a key list
-//       read through a slot table: the probe forward of the non-affix rows
-//       over the shared affix (Eq. 4 of "Affix Cache for Diffusion Large
-//       Language Models", Section 3.2) and the read-slot attention of
-//       Section 4.3 / Appendix C.1.
-//       SPLIT = 0: a workgroup owns 128 query rows (32 per wave) and every
-//                  wave walks every key (many queries: probe, recompute).
-//       SPLIT = 1: a workgroup owns 32 query rows and its four waves split
-//                  each 128-key tile into four 32-key slices; the partial
-//                  (max, sum, O) of the waves are merged at the end (decode
-//                  blocks of 32 queries).
+//   softmax(q K^T * scale) V and LSE over a key list read through a slot
+//   table: the probe forward of the non-affix rows over the shared affix
+//   (Eq. 4 of "Affix Cache for Diffusion Large Language Models", Section 3.2)
+//   and the read-slot attention of Section 4.3 / Appendix C.1, in two shapes:
+//     attn_rows_mfma   a workgroup owns 128 query rows (32 per wave) and every
+//                      wave walks every key (probe, recompute-sized sets);
+//     attn_split_mfma  a workgroup owns 32 query rows and its four waves split
+//                      each 128-key tile into four 32-key slices; the partial
+//                      (max, sum, O) of the waves are merged at the end
+//                      (decode blocks of 32 queries).
 //   colmass_mfma   the Eq. (4) weights of the masked rows recomputed as
 //       exp(q.k * scale - LSE) and summed over the rows of each request: one
 //       partial per (layer, query head, request, key); the partials are
@@ -111,8 +110,8 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a 
 
 }  // namespace
 
-template <int SPLIT>
-__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
+__global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
+  constexpr int SPLIT = 1;
   constexpr int BN = SPLIT ? 128 : 64;   // keys per LDS tile
   constexpr int RT = SPLIT ? 32 : 128;   // query rows per workgroup
   constexpr int NSUB = SPLIT ? 1 : BN / 32;
@@ -378,6 +377,217 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnP p) {
     p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
 }
 
+// Many-query attention (probe forward over the shared affix; read-slot
+// attention of recompute-sized query sets).  A workgroup owns 128 query rows
+// (32 per wave) and walks the key list in tiles of 64.  K and V tiles are
+// gathered through the slot table straight into a 2-stage LDS ring by
+// direct-to-LDS loads (no register staging); rows are stored as they sit in
+// the pool with their 16-byte chunks XOR-swizzled by row, and the V^T operands
+// of P.V come from transposing LDS reads.  Slot numbers arrive through scalar
+// loads a tile ahead, so the vector-memory counter tracks only tile loads; the
+// next tile's loads are in flight while the current one is computed, with one
+// barrier per tile.
+namespace {
+constexpr int RB = 64;                   // keys per tile
+constexpr int RSTAGES = 2;
+constexpr int ROWB = D * 2;              // bytes of one K or V row
+constexpr int RSTAGE_BYTES = RB * ROWB * 2;
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Workgroup barrier without the full memory drain __syncthreads() implies:
+// the direct-to-LDS tile loads are waited for explicitly (vmcnt) before it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
+// address lds_base + 16 * i.  Issued as asm so that the compiler does not
+// serialise later LDS reads behind it; callers wait on vmcnt themselves and
+// issue no other vector-memory loads whose results they consume meanwhile.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16-byte chunk swizzles of a 256-byte K or V row: conflict-free for the
+// MFMA operand reads of K (16 rows x one chunk) and the transposing reads of
+// V (4 rows x 2 chunks per 16 lanes)
+__device__ __forceinline__ uint32_t kswz(uint32_t row, uint32_t chunk) { return chunk ^ (row & 15u); }
+__device__ __forceinline__ uint32_t vswz2(uint32_t row, uint32_t chunk) { return chunk ^ ((row & 3u) << 2); }
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
+  __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
+  const int unit = xcd_unit(p.per_xcd);
+  if (unit >= p.n_units) return;
+  int r = unit;
+  const int t = r % p.q_tiles;
+  r /= p.q_tiles;
+  const int b = r % p.B;
+  r /= p.B;
+  const int h = r % p.n_q_heads;
+  const int n = r / p.n_q_heads;
+  const int g = h / (p.n_q_heads / p.geo.n_kv_heads);
+  const int layer = p.layer_begin + n;
+  int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
+  if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
+  if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
+  const int rbase = q0 + t * 128;
+  if (rbase >= q1) return;
+  const int nk = k1 - k0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int qrow = rbase + wave * 32 + l32;
+  const bool qvalid = qrow < q1;
+  const bool wave_live = rbase + wave * 32 < q1;
+
+  // Q as the B operand of S^T = K Q^T
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : q0)) * p.n_q_heads + h) * D + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) o[a] = f32x16{};
+
+  const char* kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
+  const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
+  const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+  const uint32_t head_off = (uint32_t)g * p.geo.page_size * ROWB;
+  // the slot table is read-only here: reading it through the constant address
+  // space lets these wave-uniform reads go through scalar loads
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(p.kv_table + k0);
+  const int ntiles = (nk + RB - 1) / RB;
+
+  // this wave loads tile rows 16*wave .. 16*wave+15 of K and of V: DMA
+  // instruction i covers rows 16*wave + 4i + lane/16, one 16-byte chunk per lane
+  int32_t sl[16];
+  auto sload = [&](int tile) {
+    const int kb = tile * RB + 16 * wave;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sl[i] = table[min(kb + i, nk - 1)];
+  };
+  auto dma = [&](int tile) {
+    char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
+    const uint32_t chunk = lane & 15;
+    const int sel = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // slots are wave-uniform (scalar registers); pick this lane's row's slot
+      const int32_t s0 = sl[4 * i], s1 = sl[4 * i + 1], s2 = sl[4 * i + 2], s3 = sl[4 * i + 3];
+      const int32_t slot = (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
+      const uint32_t row = 16 * wave + 4 * i + sel;
+      const uint32_t off = ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
+                           ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * ROWB;
+      dma16(kbase + off + kswz(row, chunk) * 16, lds_addr(st + (16 * wave + 4 * i) * ROWB));
+      dma16(vbase + off + vswz2(row, chunk) * 16, lds_addr(st + RB * ROWB + (16 * wave + 4 * i) * ROWB));
+    }
+  };
+
+  if (ntiles > 0) { sload(0); dma(0); }
+  if (ntiles > 1) sload(1);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this tile's loads have landed
+    wg_barrier();                        // ... in every wave; and every wave is done with the other stage
+    if (tile + 1 < ntiles) {
+      dma(tile + 1);
+      if (tile + 2 < ntiles) sload(tile + 2);
+    }
+    if (!wave_live) continue;
+    const int kb = tile * RB;
+    const char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
+    const char* vst = st + RB * ROWB;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const uint32_t krow = sub * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krow * ROWB + kswz(krow, 2 * c + g2) * 16)), qf[c], s[sub]);
+    }
+    if (kb + RB > nk) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[sub][i] = -INFINITY;
+    }
+    float mr = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    const float mt = mr * p.c2;
+    // rescale only when the running max grows by more than 2^8 (exact either
+    // way: O and the row sum carry the same factor)
+    if (mt > m + 8.f) {
+      const float alpha = exp2f(m - mt);
+      lsum *= alpha;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+      m = mt;
+    }
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+    const uint32_t i16 = lane & 15;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
+          lsum += pv;
+          pb[j] = (__bf16)pv;
+        }
+        // V^T operand: key slots follow the score tile's C layout
+        const uint32_t row1 = sub * 32 + 16 * hh + 4 * g2 + (i16 >> 2);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+          const uint32_t c16 = dcol >> 3, sub8 = (dcol & 7) * 2;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vst + row1 * ROWB + vswz2(row1, c16) * 16 + sub8));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vst + (row1 + 8) * ROWB + vswz2(row1 + 8, c16) * 16 + sub8));
+          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
+        }
+      }
+  }
+  if (!qvalid) return;
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (p.out) {
+    bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = a * 32 + 8 * i4 + 4 * g2;
+        u32x2 w;
+        w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
+        w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
+        *(u32x2*)(op + d) = w;
+      }
+  }
+  if (p.lse && g2 == 0)
+    p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+}
+
 // Column mass of the masked rows.  A workgroup owns 256 affix keys (64 per
 // wave, held as two B-operand tiles in registers) of one (layer, query head)
 // and streams every request's masked rows through LDS in tiles of 32.  The
@@ -529,8 +739,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
   dim3 grid(8 * p.per_xcd), block(256);
-  if (split) hipLaunchKernelGGL(attn_fwd_mfma<1>, grid, block, 0, st, p);
-  else hipLaunchKernelGGL(attn_fwd_mfma<0>, grid, block, 0, st, p);
+  if (split) hipLaunchKernelGGL(attn_split_mfma, grid, block, 0, st, p);
+  else hipLaunchKernelGGL(attn_rows_mfma, grid, block, 0, st, p);
   return hipGetLastError();
 }
 

@@ -251,15 +251,15 @@ def main():
     probe_ms_req = (stage_ms["probe_attention"] + stage_ms["probe_column_mass"] + stage_ms["topk_maps"]) / w.batch
     probe_tflops = wm["probe_flops"] / t_probe / 1e12
     traffic = measured_traffic(w.name)
-    roof = {"kernel": "attn_fwd_mfma<0> (probe attention, one launch for all layers)", "bound": "mfma",
+    roof = {"kernel": "attn_rows_mfma (probe attention, one launch for all layers)", "bound": "mfma",
             "achieved": probe_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get("attn_fwd_mfma<0>"),
+            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get("attn_rows_mfma"),
             "traffic_unit": "HBM bytes per launch", "algorithmic_per_launch": wm["probe_flops"],
             "algorithmic_bytes_per_launch": wm["probe_bytes"]}
     mapped_gbs = wm["mapped_bytes"] / t_map / 1e9
-    roof_mapped = {"kernel": "attn_fwd_mfma<1> (read-slot attention, one launch for all layers)", "bound": "hbm",
+    roof_mapped = {"kernel": "attn_split_mfma (read-slot attention, one launch for all layers)", "bound": "hbm",
                    "achieved": mapped_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": mapped_gbs / PEAK_HBM_GBS,
-                   "traffic": traffic.get("attn_fwd_mfma<1>"), "traffic_unit": "HBM bytes per launch",
+                   "traffic": traffic.get("attn_split_mfma"), "traffic_unit": "HBM bytes per launch",
                    "algorithmic_per_launch": wm["mapped_bytes"]}
     scatter_gbs = wm["scatter_bytes"] / (stage_ms["admission_scatter"] * 1e-3) / 1e9
     out = {
