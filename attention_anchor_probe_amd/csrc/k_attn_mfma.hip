@@ -478,22 +478,41 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sl[i] = table[min(kb + i, nk - 1)];
   };
+  // per-lane parts of the DMA addresses: lane/16 picks the row of the 4-row
+  // group, lane%16 the LDS chunk; the global chunk is its swizzle
+  const int sel = lane >> 4;
+  uint32_t kchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
+  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
+  const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
   auto dma = [&](int tile) {
-    char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
-    const uint32_t chunk = lane & 15;
-    const int sel = lane >> 4;
+    const uint32_t st = lds0 + (tile % RSTAGES) * RSTAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // slots are wave-uniform (scalar registers); pick this lane's row's slot
       const int32_t s0 = sl[4 * i], s1 = sl[4 * i + 1], s2 = sl[4 * i + 2], s3 = sl[4 * i + 3];
       const int32_t slot = (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
-      const uint32_t row = 16 * wave + 4 * i + sel;
       const uint32_t off = ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
                            ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * ROWB;
-      dma16(kbase + off + kswz(row, chunk) * 16, lds_addr(st + (16 * wave + 4 * i) * ROWB));
-      dma16(vbase + off + vswz2(row, chunk) * 16, lds_addr(st + RB * ROWB + (16 * wave + 4 * i) * ROWB));
+      dma16(kbase + off + kchunk[i], st + 4 * i * ROWB);
+      dma16(vbase + off + vchunk, st + RB * ROWB + 4 * i * ROWB);
     }
   };
+
+  // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
+  // sub-block adds compile-time multiples of 16 rows, which keep the swizzle)
+  uint32_t krd[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) krd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
+  const uint32_t i16 = lane & 15;
+  uint32_t vrd[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t row = 4 * g2 + (i16 >> 2);
+    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+    vrd[a] = RB * ROWB + row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+  }
 
   if (ntiles > 0) { sload(0); dma(0); }
   if (ntiles > 1) sload(1);
@@ -507,15 +526,12 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
     if (!wave_live) continue;
     const int kb = tile * RB;
     const char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
-    const char* vst = st + RB * ROWB;
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const uint32_t krow = sub * 32 + l32;
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krow * ROWB + kswz(krow, 2 * c + g2) * 16)), qf[c], s[sub]);
-    }
+        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
     if (kb + RB > nk) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -542,7 +558,6 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
       m = mt;
     }
     const float nm = (m == -INFINITY) ? 0.f : -m;
-    const uint32_t i16 = lane & 15;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -554,16 +569,13 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
           lsum += pv;
           pb[j] = (__bf16)pv;
         }
-        // V^T operand: key slots follow the score tile's C layout
-        const uint32_t row1 = sub * 32 + 16 * hh + 4 * g2 + (i16 >> 2);
+        // V^T operand: key slots follow the score tile's C layout (keys
+        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-          const uint32_t c16 = dcol >> 3, sub8 = (dcol & 7) * 2;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(vst + row1 * ROWB + vswz2(row1, c16) * 16 + sub8));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(vst + (row1 + 8) * ROWB + vswz2(row1 + 8, c16) * 16 + sub8));
+          const char* vp = st + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
           o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
         }
       }
