@@ -100,30 +100,27 @@ __device__ __forceinline__ int xcd_unit(int per_xcd) {
   return (i & 7) * per_xcd + (i >> 3);
 }
 
-// Swizzle of the 8-key groups in a transposed V row (spreads the rows of one
-// column over LDS banks for both the transposing writes and the MFMA reads).
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
-
-// low 16 bits of the two words packed: (a & 0xffff) | (b << 16)
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
 }  // namespace
 
+// 16-byte chunk swizzle of a 256-byte V row: conflict-free for row-wise
+// 16-byte writes and for the transposing reads (4 rows x 2 chunks per 16 lanes)
+__device__ __forceinline__ uint32_t vswz_rows(uint32_t row, uint32_t chunk) { return chunk ^ ((row & 3u) << 2); }
+
+// bf16x4 view of LDS for the transposing reads
+typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4s lds_bf16x4s;
+
 __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
-  constexpr int SPLIT = 1;
-  constexpr int BN = SPLIT ? 128 : 64;   // keys per LDS tile
-  constexpr int RT = SPLIT ? 32 : 128;   // query rows per workgroup
-  constexpr int NSUB = SPLIT ? 1 : BN / 32;
-  constexpr int KLD = BN * 16 / 256;     // 16-byte K loads per thread per tile
-  constexpr int VQ = BN / 4 * 16 / 256;  // (4 keys x 8 d) V items per thread per tile
+  constexpr int BN = 128;                // keys per LDS tile; wave w computes keys 32w .. 32w+31
+  constexpr int KLD = BN * 16 / 256;     // 16-byte K (and V) row pieces per thread per tile
   constexpr int KS_BYTES = BN * KS * 2;
-  constexpr int VT_BYTES = D * BN * 2;
-  constexpr int MERGE_BYTES = SPLIT ? (4 * 4 * 16 * 64 * 4 + 2 * 4 * 64 * 4) : 0;
-  constexpr int LDS_BYTES = (KS_BYTES + VT_BYTES) > MERGE_BYTES ? (KS_BYTES + VT_BYTES) : MERGE_BYTES;
+  constexpr int VR_BYTES = BN * D * 2;
+  constexpr int MERGE_BYTES = 4 * 4 * 16 * 64 * 4 + 2 * 4 * 64 * 4;
+  constexpr int LDS_BYTES = (KS_BYTES + VR_BYTES) > MERGE_BYTES ? (KS_BYTES + VR_BYTES) : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   bf16_t* Ks = (bf16_t*)smem;
-  bf16_t* Vt = (bf16_t*)(smem + KS_BYTES);
+  char* Vr = smem + KS_BYTES;  // V rows as stored in the pool, 16-byte chunks swizzled by row
 
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
@@ -139,15 +136,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
   int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
   if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
   if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
-  const int rbase = q0 + t * RT;
+  const int rbase = q0 + t * 32;
   if (rbase >= q1) return;
   const int nk = k1 - k0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
-  const int qrow = SPLIT ? rbase + l32 : rbase + wave * 32 + l32;
+  const int qrow = rbase + l32;
   const bool qvalid = qrow < q1;
-  const bool wave_live = SPLIT ? true : (rbase + wave * 32 < q1);
 
   // Q as the B operand of S^T = K Q^T
   bf16x8 qf[8];
@@ -162,8 +158,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  u32x4 kreg[KLD], vreg[VQ * 4];
-  uint32_t koff[KLD], voff[VQ * 4];
+  u32x4 kreg[KLD], vreg[KLD];
+  uint32_t koff[KLD];
   const int ntiles = (nk + BN - 1) / BN;
   // one layer of the pool is addressed from a scalar base with 32-bit byte offsets
   const char* kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
@@ -175,58 +171,44 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
            ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * (D * 2);
   };
 
-  // Slots of a tile are loaded one tile ahead of its K/V rows, so a row load
-  // never waits on the table load that names it.  Keys past the end are
-  // clamped to the last key (their scores are masked to -inf below, so their
-  // rows only ever meet a zero weight).
+  // Thread tid moves 16-byte piece tid%16 of rows tid/16 + 16e of the tile,
+  // for K and for V.  Slots of a tile are loaded one tile ahead of its rows,
+  // so a row load never waits on the table load that names it.  Keys past the
+  // end are clamped to the last key (their scores are masked to -inf below,
+  // so their rows only ever meet a zero weight).
   auto sload = [&](int tile) {
     const int kb = tile * BN;
 #pragma unroll
-    for (int e = 0; e < KLD; ++e) {
-      const int key = min(kb + (tid >> 4) + 16 * e, nk - 1);
-      koff[e] = (uint32_t)p.kv_table[k0 + key];
-    }
-#pragma unroll
-    for (int e = 0; e < VQ; ++e)
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int key = min(kb + 4 * ((tid >> 4) + 16 * e) + k4, nk - 1);
-        voff[e * 4 + k4] = (uint32_t)p.kv_table[k0 + key];
-      }
+    for (int e = 0; e < KLD; ++e) koff[e] = (uint32_t)p.kv_table[k0 + min(kb + (tid >> 4) + 16 * e, nk - 1)];
   };
   auto dload = [&]() {
 #pragma unroll
-    for (int e = 0; e < KLD; ++e) kreg[e] = *(const u32x4*)(kbase + slot_off((int32_t)koff[e]));
-#pragma unroll
-    for (int e = 0; e < VQ * 4; ++e) vreg[e] = *(const u32x4*)(vbase + slot_off((int32_t)voff[e]));
+    for (int e = 0; e < KLD; ++e) {
+      const uint32_t off = slot_off((int32_t)koff[e]);
+      kreg[e] = *(const u32x4*)(kbase + off);
+      vreg[e] = *(const u32x4*)(vbase + off);
+    }
   };
-
   auto lstore = [&]() {
+    const uint32_t dc = tid & 15;
 #pragma unroll
     for (int e = 0; e < KLD; ++e) {
-      const int u = tid + 256 * e;
-      const int key = u >> 4, dc = u & 15;
+      const uint32_t key = (tid >> 4) + 16 * e;
       *(u32x4*)(Ks + key * KS + dc * 8) = kreg[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VQ; ++e) {
-      const int u = tid + 256 * e;
-      const int kq = u >> 4, dc = u & 15;
-      const int chunk = kq >> 2, q4 = kq & 3;
-      const int grp = chunk * 2 + (q4 & 1), w0 = (q4 >> 1) * 4;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int d = dc * 8 + dd;
-        const int wd = dd >> 1;
-        uint32_t a0 = vreg[e * 4 + 0][wd], a1 = vreg[e * 4 + 1][wd];
-        uint32_t a2 = vreg[e * 4 + 2][wd], a3 = vreg[e * 4 + 3][wd];
-        u32x2 pk;
-        if (dd & 1) { pk[0] = pack_hi(a0, a1); pk[1] = pack_hi(a2, a3); }
-        else { pk[0] = pack_lo(a0, a1); pk[1] = pack_lo(a2, a3); }
-        *(u32x2*)(Vt + d * BN + (((grp ^ vswz(d)) << 3) | w0)) = pk;
-      }
+      *(u32x4*)(Vr + key * (D * 2) + vswz_rows(key, dc) * 16) = vreg[e];
     }
   };
+
+  // per-lane offsets of the transposing V reads (keys 4*g + 0..3 and
+  // 8 + 4*g + 0..3 of each 16-key block, d column a*32 + lane%32)
+  const uint32_t i16 = lane & 15;
+  uint32_t vrd[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t row = wave * 32 + 4 * g2 + (i16 >> 2);
+    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+    vrd[a] = row * (D * 2) + vswz_rows(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+  }
 
   if (ntiles > 0) {
     sload(0);
@@ -241,33 +223,23 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
       dload();
       if (tile + 2 < ntiles) sload(tile + 2);
     }
-    if (!wave_live) continue;
     const int kb = tile * BN;
-    f32x16 s[NSUB];
+    f32x16 s = f32x16{};
+    {
+      const bf16_t* kp = Ks + (wave * 32 + l32) * KS + g2 * 8;
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-      const int sub = SPLIT ? wave : st;
-      s[st] = f32x16{};
-      const bf16_t* kp = Ks + (sub * 32 + l32) * KS + g2 * 8;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s[st] = mfma(as_bf16x8(*(const u32x4*)(kp + c * 16)), qf[c], s[st]);
+      for (int c = 0; c < 8; ++c) s = mfma(as_bf16x8(*(const u32x4*)(kp + c * 16)), qf[c], s);
     }
     // keys past the end (tail tile only) get -inf; the running max m lives in
     // the scaled log2 domain, c2 > 0, so max(s) * c2 is the scaled tile max
     if (kb + BN > nk) {
 #pragma unroll
-      for (int st = 0; st < NSUB; ++st) {
-        const int sub = SPLIT ? wave : st;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[st][i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (kb + wave * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[i] = -INFINITY;
     }
     float mr = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[st][i]);
+    for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[i]);
     mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
     const float mt = mr * p.c2;
     // rescale only when the running max grows by more than 2^8 (exact either
@@ -283,51 +255,25 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
     }
     const float nm = (m == -INFINITY) ? 0.f : -m;
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-      const int sub = SPLIT ? wave : st;
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 pb;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pb;
+      for (int j = 0; j < 8; ++j) {
+        const float pv = fast_exp2(fmaf(s[8 * hh + j], p.c2, nm));
+        lsum += pv;
+        pb[j] = (__bf16)pv;
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = fast_exp2(fmaf(s[st][8 * hh + j], p.c2, nm));
-          lsum += pv;
-          pb[j] = (__bf16)pv;
-        }
-        const int grp = sub * 4 + hh * 2 + g2;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int d = a * 32 + l32;
-          const bf16x8 va = as_bf16x8(*(const u32x4*)(Vt + d * BN + ((grp ^ vswz(d)) << 3)));
-          o[a] = mfma(va, pb, o[a]);
-        }
+      for (int a = 0; a < 4; ++a) {
+        const char* vp = Vr + vrd[a] + 16 * hh * (D * 2);
+        const bf16x4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4s*)vp);
+        const bf16x4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4s*)(vp + 8 * (D * 2)));
+        o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
       }
     }
   }
 
-  if (!SPLIT) {
-    if (!qvalid) return;
-    const float lt = lsum + __shfl_xor(lsum, 32, 64);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (p.out) {
-      bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = a * 32 + 8 * i4 + 4 * g2;
-          u32x2 w;
-          w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
-          w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
-          *(u32x2*)(op + d) = w;
-        }
-    }
-    if (p.lse && g2 == 0)
-      p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-    return;
-  }
-
-  // SPLIT: merge the four waves' partial results through LDS
+  // merge the four waves' partial results through LDS
   float* red = (float*)smem;                      // [wave][a][i][lane]
   float* mw = red + 4 * 4 * 16 * 64;              // [wave][lane]
   float* lw = mw + 4 * 64;                        // [wave][lane]
