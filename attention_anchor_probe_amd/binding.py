@@ -64,6 +64,10 @@ _SIG = {
     "acache_mapped_attention_workspace_bytes": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
                                  _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_mapped_attention_shared_workspace_bytes": ([ctypes.POINTER(KVPool), _I, _I, _I, _I, _I, _I, _I,
+                                                        ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                        _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "acache_validate_slots": ([_P, _I, _P, _P, _I, _I, _I, ctypes.POINTER(_I)], ctypes.c_int),
 }
 EXPORTS = tuple(_SIG)
@@ -264,6 +268,44 @@ def acache_mapped_attention(pool_k, pool_v, q, q_offsets, read_slot, kv_offsets,
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention", st)
+
+
+def acache_mapped_attention_shared_workspace_bytes(pool_k, pool_v, *, B, n_q, max_q_per_req, n_q_heads, n_layers,
+                                                   max_kv_per_req, L):
+    pool = make_pool(pool_k, pool_v)
+    ws_bytes = ctypes.c_size_t()
+    _check("acache_mapped_attention_shared_workspace_bytes",
+           _lib().acache_mapped_attention_shared_workspace_bytes(
+               ctypes.byref(pool), int(B), int(n_q), int(max_q_per_req), int(n_q_heads), int(n_layers),
+               int(max_kv_per_req), int(L), ctypes.byref(ws_bytes)))
+    return ws_bytes.value
+
+
+def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_offsets, shared_slots, out, *,
+                                   affix_l, max_q_per_req, max_kv_per_req, lse=None, layer_begin=0, scale=None,
+                                   workspace=None, stream=None):
+    """Read-slot attention of a batch sharing one affix (same result as
+    acache_mapped_attention).  q/out: [n_layers][n_q][Hq][d]; shared_slots [L]."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_q, hq, d = q.shape
+    B = q_offsets.numel() - 1
+    L = shared_slots.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        nb = acache_mapped_attention_shared_workspace_bytes(
+            pool_k, pool_v, B=B, n_q=n_q, max_q_per_req=max_q_per_req, n_q_heads=hq, n_layers=n_layers,
+            max_kv_per_req=max_kv_per_req, L=L)
+        if nb > 0:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    st = _lib().acache_mapped_attention_shared(
+        ctypes.byref(pool), _dev(q, pool_k.dtype), _dev(q_offsets, torch.int32), n_q, int(max_q_per_req),
+        _dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32), int(max_kv_per_req),
+        _dev(shared_slots, torch.int32), int(affix_l), L, B, hq, layer_begin, n_layers, float(scale),
+        _dev(out, pool_k.dtype), _dev(lse, torch.float32),
+        _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
+        _stream(stream))
+    _check("acache_mapped_attention_shared", st)
 
 
 def acache_validate_slots(slots, page_owner, n_pages, page_size, owner=None, distinct=True):

@@ -361,6 +361,104 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
   return status_of(e);
 }
 
+namespace {
+// workspace of the two-pass shared-affix attention (256-byte aligned parts)
+struct SharedWs {
+  bool two_pass = false;
+  int excl_words = 0, stride = 0;
+  size_t priv = 0, counts = 0, excl = 0, total = 0;
+};
+
+SharedWs shared_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t n_q, int32_t max_q, int32_t n_q_heads,
+                          int32_t n_layers, int32_t max_kv, int32_t L) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  SharedWs w;
+  w.two_pass = mfma_supported(pool->dtype, pool->head_dim) && max_q <= 32;
+  if (!w.two_pass) return w;
+  w.excl_words = 2 * ((L + 63) / 64);
+  size_t off = 0;
+  w.stride = (max_kv + kSharedPrivTile - 1) / kSharedPrivTile * kSharedPrivTile;
+  w.priv = off;
+  off += up((size_t)B * w.stride * 4);
+  w.counts = off;
+  off += up((size_t)B * 4);
+  w.excl = off;
+  off += up((size_t)B * w.excl_words * 4);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+int acache_mapped_attention_shared_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t n_q,
+                                                   int32_t max_q_per_req, int32_t n_q_heads, int32_t n_layers,
+                                                   int32_t max_kv_per_req, int32_t L, size_t* bytes) {
+  int st;
+  if (!bytes) return ACACHE_EINVAL;
+  if ((st = check_pool(pool))) return st;
+  if (B < 0 || n_q < 0 || max_q_per_req < 0 || n_q_heads < 0 || n_layers < 0 || max_kv_per_req < 0 || L < 0)
+    return ACACHE_EINVAL;
+  *bytes = shared_ws_layout(pool, B, n_q, max_q_per_req, n_q_heads, n_layers, max_kv_per_req, L).total;
+  return ACACHE_OK;
+}
+
+int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
+                                   int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
+                                   int32_t max_kv_per_req, const int32_t* shared_slots, int32_t affix_l, int32_t L,
+                                   int32_t B, int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if (affix_l < 0 || L < 0) return ACACHE_EINVAL;
+  if (L > 0 && !shared_slots) return ACACHE_EINVAL;
+  const SharedWs w = shared_ws_layout(pool, B < 0 ? 0 : B, n_q < 0 ? 0 : n_q, max_q_per_req, n_q_heads < 0 ? 0 : n_q_heads,
+                                      n_layers < 0 ? 0 : n_layers, max_kv_per_req < 0 ? 0 : max_kv_per_req, L);
+  if (!w.two_pass)
+    return acache_mapped_attention(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                   n_q_heads, layer_begin, n_layers, scale, out, lse, nullptr, 0, stream);
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if ((st = check_heads(pool, n_q_heads))) return st;
+  if (B < 0 || n_q < 0 || max_q_per_req < 0 || max_q_per_req > n_q || max_kv_per_req < 0) return ACACHE_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
+  if (B > 65535) return ACACHE_ESHAPE;
+  if ((long long)B * (max_kv_per_req + kSharedPrivTile) >= (1ll << 31)) return ACACHE_ESHAPE;
+  if (B == 0 || n_q == 0 || n_layers == 0) return ACACHE_OK;
+  if (!q || !q_offsets || !kv_offsets || !out) return ACACHE_EINVAL;
+  if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return ACACHE_EALIGN;
+  if (!workspace || workspace_bytes < w.total) return ACACHE_EWORKSPACE;
+  if (!aligned16(workspace)) return ACACHE_EALIGN;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_shared_plan(read_slot, kv_offsets, shared_slots, B, affix_l, L, max_kv_per_req, w.stride,
+                                    kSharedPrivTile, (int32_t*)(ws + w.priv), (int32_t*)(ws + w.counts),
+                                    (uint32_t*)(ws + w.excl), w.excl_words, s);
+  if (e != hipSuccess) return status_of(e);
+  SharedAttnArgs a;
+  a.q = q;
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.geo = geom_of(pool);
+  a.q_offsets = q_offsets;
+  a.n_q = n_q;
+  a.max_q = max_q_per_req;
+  a.shared_slots = shared_slots;
+  a.L = L;
+  a.excl = (const uint32_t*)(ws + w.excl);
+  a.excl_words = w.excl_words;
+  a.priv_slots = (const int32_t*)(ws + w.priv);
+  a.priv_counts = (const int32_t*)(ws + w.counts);
+  a.priv_stride = w.stride;
+  a.B = B;
+  a.n_q_heads = n_q_heads;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  return status_of(launch_attn_mfma_shared(a, s));
+}
+
 int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner, const int32_t* page_owner,
                           int32_t n_pages, int32_t page_size, int32_t distinct, int32_t* bad_index) {
   if (n < 0 || n_pages <= 0 || page_size <= 0 || (page_size & (page_size - 1))) return ACACHE_EINVAL;

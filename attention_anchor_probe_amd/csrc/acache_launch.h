@@ -33,6 +33,35 @@ struct AttnArgs {
   float* lse;
 };
 
+// Read-slot attention for decode blocks (at most 32 rows per request) whose
+// read tables mostly route the affix to the shared region: every request's
+// rows attend to the affix keys shared_slots[0 .. L) minus the keys flagged
+// in excl (read once per group of four requests) and to their own list
+// priv_slots[b * priv_stride .. + priv_counts[b]), in one softmax.
+struct SharedAttnArgs {
+  const void* q;
+  const void* pool_k;
+  const void* pool_v;
+  PoolGeom geo;
+  const int32_t* q_offsets;
+  int n_q;
+  int max_q;
+  const int32_t* shared_slots;
+  int L;
+  const uint32_t* excl;
+  int excl_words;
+  const int32_t* priv_slots;
+  const int32_t* priv_counts;
+  int priv_stride;
+  int B;
+  int n_q_heads;
+  int layer_begin;
+  int n_layers;
+  float scale;
+  void* out;
+  float* lse;
+};
+
 // Column mass of the masked rows (Eq. 4 weights summed over heads and rows)
 // into partial[n][b][j].
 struct ColmassArgs {
@@ -56,6 +85,15 @@ struct ColmassArgs {
 
 hipError_t launch_topk(const float* scores, int B, int L, int K, int affix_l, int32_t* anchors, hipStream_t st);
 hipError_t launch_maps(const int32_t* anchors, const acache_map_args& a, hipStream_t st);
+// Per request b: priv_slots[b * stride ..] = read slots of the positions not
+// read from the shared region (ascending, padded with the last one to a
+// multiple of pad entries), priv_counts[b] their number, and the exclusion
+// bits of the affix keys (see SharedAttnArgs).  Positions past max_kv are
+// ignored; stride >= max_kv rounded up to a multiple of pad.
+hipError_t launch_shared_plan(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* shared_slots,
+                              int B, int affix_l, int L, int max_kv, int stride, int pad, int32_t* priv_slots,
+                              int32_t* priv_counts, uint32_t* excl, int excl_words, hipStream_t st);
+constexpr int kSharedPrivTile = 32;  // private-list tile of attn_shared_mfma
 hipError_t launch_block_slots(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* block_start,
                               int B, int block_len, int32_t* dst, hipStream_t st);
 hipError_t launch_scatter(void* pool_k, void* pool_v, const void* k_src, const void* v_src, const int32_t* dst,
@@ -69,6 +107,7 @@ hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int 
 // bf16, head_dim 128, MFMA kernels (k_attn_mfma.hip)
 bool mfma_supported(int dtype, int head_dim);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st);
 hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st);
 
 }  // namespace acache

@@ -10,7 +10,10 @@
 //     attn_split_mfma  a workgroup owns 32 query rows and its four waves split
 //                      each 128-key tile into four 32-key slices; the partial
 //                      (max, sum, O) of the waves are merged at the end
-//                      (decode blocks of 32 queries).
+//                      (decode blocks of 32 queries);
+//     attn_shared_mfma decode blocks of four requests that share the affix:
+//                      the affix tiles are loaded once for the four, each
+//                      wave then streams its own request's other keys.
 //   colmass_mfma   the Eq. (4) weights of the masked rows recomputed as
 //       exp(q.k * scale - LSE) and summed over the rows of each request: one
 //       partial per (layer, query head, request, key); the partials are
@@ -23,6 +26,8 @@
 // A contraction only needs A and B to agree on what each K-slot means, so
 // the head dimension is split as d = 16*c + 8*g + j for MFMA step c, and the
 // key slots of the P.V product follow the C layout of the score tile.
+#include <type_traits>
+
 #include "acache_dev.h"
 #include "acache_launch.h"
 
@@ -58,6 +63,15 @@ struct AttnP {
   float* lse;
   int n_units;
   int per_xcd;
+  // attn_shared_mfma only: bit j of excl[b * excl_words + j / 32] set = affix
+  // key j is not read from the shared region by request b (the padding up to
+  // whole 64-key tiles is set too); request b's other read slots are
+  // priv_table[b * kv_stride .. + kv_counts[b])
+  const uint32_t* excl;
+  int excl_words;
+  const int32_t* priv_table;
+  const int32_t* kv_counts;
+  int kv_stride;
 };
 
 struct ColP {
@@ -338,6 +352,8 @@ constexpr int RB = 64;                   // keys per tile
 constexpr int RSTAGES = 2;
 constexpr int ROWB = D * 2;              // bytes of one K or V row
 constexpr int RSTAGE_BYTES = RB * ROWB * 2;
+constexpr int PTILE = kSharedPrivTile;   // keys per private tile of attn_shared_mfma (per wave)
+static_assert(4 * PTILE * ROWB * 2 <= RSTAGES * RSTAGE_BYTES, "private regions fit the tile ring");
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -546,6 +562,282 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
     p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
+// Read-slot attention of decode blocks whose requests share one affix
+// (Section 4.3 and Appendix C.1, with the single shared region of
+// Section 4.1).  A workgroup owns one (layer, query head) and four requests;
+// wave w owns the (at most 32) query rows of request 4t + w.  Two phases feed
+// one online softmax per row:
+//   shared   the affix keys as one tile list for the four requests, loaded
+//            once per workgroup as in attn_rows_mfma; each wave drops the
+//            keys its request does not read from the shared region;
+//   private  each wave streams the rest of its request's read slots through
+//            its own 16 KB of LDS in 32-key tiles, refilling K and V
+//            separately so the next tile's loads overlap this tile's math.
+// Workgroups of odd unit index run the phases in the other order, so that
+// co-resident workgroups mix MFMA-bound and memory-bound work.
+__global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
+  __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
+  typedef const __attribute__((address_space(4))) int32_t* sc_i32;
+  typedef const __attribute__((address_space(4))) uint32_t* sc_u32;
+  const int unit = xcd_unit(p.per_xcd);
+  if (unit >= p.n_units) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g2 = lane >> 5, l32 = lane & 31;
+  int r = unit;
+  const int t = r % p.q_tiles;
+  r /= p.q_tiles;
+  const int h = r % p.n_q_heads;
+  const int n = r / p.n_q_heads;
+  const int g = h / (p.n_q_heads / p.geo.n_kv_heads);
+  const int layer = p.layer_begin + n;
+  const int b = 4 * t + wave;  // wave-uniform
+  int q0 = 0, q1 = 0;
+  if (b < p.B) {
+    q0 = p.q_offsets[b];
+    q1 = min(p.q_offsets[b + 1], q0 + 32);
+  }
+  const int qrow = q0 + l32;
+  const bool qvalid = qrow < q1;
+  const bool wave_live = q1 > q0;
+
+  // Q as the B operand of S^T = K Q^T
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : 0)) * p.n_q_heads + h) * D + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) o[a] = f32x16{};
+
+  const char* kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
+  const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
+  const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+  const uint32_t head_off = (uint32_t)g * p.geo.page_size * ROWB;
+  auto slot_off = [&](int32_t slot) -> uint32_t {
+    return ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
+           ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * ROWB;
+  };
+  // DMA instruction i moves rows 4i + lane/16 (of a 16- or 32-row block),
+  // one 16-byte chunk per lane; the global chunk is the swizzle of the LDS one
+  const int sel = lane >> 4;
+  uint32_t kchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;
+  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;
+  auto pick = [&](int32_t s0, int32_t s1, int32_t s2, int32_t s3) {
+    return (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
+  };
+  uint32_t krd[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) krd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
+  const uint32_t i16 = lane & 15;
+  uint32_t vrd[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t row = 4 * g2 + (i16 >> 2);
+    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+    vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+  }
+
+  // online-softmax update with NS 32-key score blocks (C layout) and the
+  // P.V product with V^T read from the V rows at vst
+  auto update = [&](auto ns, f32x16* s, const char* vst) {
+    constexpr int NS = decltype(ns)::value;
+    float mr = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    const float mt = mr * p.c2;
+    if (mt > m + 8.f) {  // lazy rescale, exact either way
+      const float alpha = exp2f(m - mt);
+      lsum *= alpha;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+      m = mt;
+    }
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
+          lsum += pv;
+          pb[j] = (__bf16)pv;
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
+        }
+      }
+  };
+
+  // ---- shared phase: workgroup-wide 64-key tiles of the affix, two stages
+  auto shared_phase = [&]() {
+    const int nk = p.n_kv;
+    if (nk <= 0) return;
+    sc_i32 table = (sc_i32)p.kv_table;
+    sc_u32 exw = (sc_u32)(p.excl + (size_t)min(b, p.B - 1) * p.excl_words);
+    const int ntiles = (nk + RB - 1) / RB;
+    int32_t sl[16];
+    uint32_t exn0 = 0, exn1 = 0;
+    auto sload = [&](int tile) {
+      const int kb = tile * RB + 16 * wave;
+      if (kb + 16 <= nk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sl[i] = table[kb + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sl[i] = table[min(kb + i, nk - 1)];
+      }
+    };
+    auto xload = [&](int tile) {
+      exn0 = exw[2 * tile];
+      exn1 = exw[2 * tile + 1];
+    };
+    const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
+    auto dma = [&](int tile) {
+      const uint32_t st = lds0 + (tile % RSTAGES) * RSTAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = slot_off(pick(sl[4 * i], sl[4 * i + 1], sl[4 * i + 2], sl[4 * i + 3]));
+        dma16(kbase + off + kchunk[i], st + 4 * i * ROWB);
+        dma16(vbase + off + vchunk, st + RB * ROWB + 4 * i * ROWB);
+      }
+    };
+    sload(0);
+    dma(0);
+    xload(0);
+    if (ntiles > 1) sload(1);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this tile's loads have landed
+      wg_barrier();                        // ... in every wave; and every wave is done with the other stage
+      const uint32_t ex0 = exn0, ex1 = exn1;
+      if (tile + 1 < ntiles) {
+        dma(tile + 1);
+        if (tile + 2 < ntiles) sload(tile + 2);
+        xload(tile + 1);
+      }
+      if (!wave_live) continue;
+      const char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+      // dropped keys (and the padding past the affix) score -inf; lane half
+      // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
+      if ((ex0 | ex1) != 0u) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const uint32_t wl = (sub ? ex1 : ex0) >> (4 * g2);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((wl >> (8 * (i >> 2) + (i & 3))) & 1u) s[sub][i] = -INFINITY;
+        }
+      }
+      update(std::integral_constant<int, 2>{}, s, st + RB * ROWB);
+    }
+  };
+
+  // ---- private phase: this wave's own 32-key tiles, no workgroup barriers
+  auto private_phase = [&]() {
+    if (!wave_live) return;
+    const int cnt = ((sc_i32)p.kv_counts)[b];
+    if (cnt <= 0) return;
+    sc_i32 ptab = (sc_i32)(p.priv_table + (size_t)b * p.kv_stride);
+    const char* reg = smem + wave * (PTILE * ROWB * 2);  // K rows, then V rows
+    const uint32_t kdst = lds_addr(reg), vdst = kdst + PTILE * ROWB;
+    const int nt = (cnt + PTILE - 1) / PTILE;
+    int32_t ps[PTILE];
+    // the lists are padded with valid slots to whole tiles
+    auto pload = [&](int tile) {
+      const int kb = tile * PTILE;
+#pragma unroll
+      for (int i = 0; i < PTILE; ++i) ps[i] = ptab[kb + i];
+    };
+    auto dma_k = [&]() {
+#pragma unroll
+      for (int i = 0; i < PTILE / 4; ++i)
+        dma16(kbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
+              kdst + 4 * i * ROWB);
+    };
+    auto dma_v = [&]() {
+#pragma unroll
+      for (int i = 0; i < PTILE / 4; ++i)
+        dma16(vbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
+              vdst + 4 * i * ROWB);
+    };
+    pload(0);
+    dma_k();
+    dma_v();
+    for (int tile = 0; tile < nt; ++tile) {
+      const bool more = tile + 1 < nt;
+      if (more) pload(tile + 1);
+      __builtin_amdgcn_s_waitcnt(0x3F78);  // vmcnt(8): K of this tile has landed (its V may not have)
+      f32x16 s[1] = {f32x16{}};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[0] = mfma(as_bf16x8(*(const u32x4*)(reg + krd[c])), qf[c], s[0]);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): K reads (and the next slots) are done
+      if (more) dma_k();
+      const int kb = tile * PTILE;
+      if (kb + PTILE > cnt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb + 8 * (i >> 2) + 4 * g2 + (i & 3) >= cnt) s[0][i] = -INFINITY;
+      }
+      if (more) __builtin_amdgcn_s_waitcnt(0x3F78);  // vmcnt(8): V of this tile has landed
+      else __builtin_amdgcn_s_waitcnt(0x3F70);
+      update(std::integral_constant<int, 1>{}, s, reg + PTILE * ROWB);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): V reads are done
+      if (more) dma_v();
+    }
+  };
+
+  if (unit & 1) {
+    private_phase();
+    wg_barrier();  // every wave is done with its private region before the shared tiles land
+    shared_phase();
+  } else {
+    shared_phase();
+    wg_barrier();  // every wave is done with the shared tiles before its private loads land
+    private_phase();
+  }
+
+  if (!qvalid) return;
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const size_t row = ((size_t)n * p.n_q + qrow) * p.n_q_heads + h;
+  bf16_t* op = p.out + row * D;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = a * 32 + 8 * i4 + 4 * g2;
+      u32x2 w;
+      w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
+      w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
+      *(u32x2*)(op + d) = w;
+    }
+  if (p.lse && g2 == 0) p.lse[row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+}
+
 // Column mass of the masked rows.  A workgroup owns 256 affix keys (64 per
 // wave, held as two B-operand tiles in registers) of one (layer, query head)
 // and streams every request's masked rows through LDS in tiles of 32.  The
@@ -699,6 +991,40 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   dim3 grid(8 * p.per_xcd), block(256);
   if (split) hipLaunchKernelGGL(attn_split_mfma, grid, block, 0, st, p);
   else hipLaunchKernelGGL(attn_rows_mfma, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st) {
+  if (a.max_q > 32) return hipErrorInvalidValue;
+  AttnP p{};
+  p.q = (const bf16_t*)a.q;
+  p.pool_k = (const bf16_t*)a.pool_k;
+  p.pool_v = (const bf16_t*)a.pool_v;
+  p.geo = a.geo;
+  p.q_offsets = a.q_offsets;
+  p.n_q = a.n_q;
+  p.q_tiles = (a.B + 3) / 4;
+  p.kv_table = a.shared_slots;
+  p.n_kv = a.L;
+  p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
+  if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
+  p.B = a.B;
+  p.n_q_heads = a.n_q_heads;
+  p.layer_begin = a.layer_begin;
+  p.c2 = a.scale * kLog2e;
+  p.out = (bf16_t*)a.out;
+  p.lse = a.lse;
+  p.excl = a.excl;
+  p.excl_words = a.excl_words;
+  p.priv_table = a.priv_slots;
+  p.kv_counts = a.priv_counts;
+  p.kv_stride = a.priv_stride;
+  const long long units = (long long)a.n_layers * a.n_q_heads * p.q_tiles;
+  if (units == 0) return hipSuccess;
+  if (units > (1ll << 30)) return hipErrorInvalidValue;
+  p.n_units = (int)units;
+  p.per_xcd = (int)((units + 7) / 8);
+  hipLaunchKernelGGL(attn_shared_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

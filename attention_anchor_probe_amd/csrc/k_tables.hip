@@ -203,6 +203,69 @@ hipError_t launch_maps(const int32_t* anchors, const acache_map_args& a, hipStre
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Plan of the two-pass decode attention: a request's read list (Section 4.3
+// read-slot map) is split into the affix positions it reads from the shared
+// region, as exclusion bits over the affix, and the ascending list of the
+// slots of every other position.  One workgroup per request.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kTopkThreads) void shared_plan_kernel(
+    const int32_t* __restrict__ read_slot, const int32_t* __restrict__ kv_offsets,
+    const int32_t* __restrict__ shared_slots, int affix_l, int L, int max_kv, int stride, int pad,
+    int32_t* __restrict__ priv_slots, int32_t* __restrict__ priv_counts, uint32_t* __restrict__ excl,
+    int excl_words) {
+  __shared__ uint32_t wave_tot[kTopkWaves + 1];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = kv_offsets[b];
+  const int T = min(kv_offsets[b + 1] - k0, max_kv);
+  const int32_t* rs = read_slot + k0;
+  // affix key j is dropped from the shared pass unless position affix_l + j
+  // exists and reads shared_slots[j]; the padding up to a whole 64-key tile
+  // is dropped too
+  uint32_t* ex = excl + (size_t)b * excl_words;
+  for (int j0 = wave * 64; j0 < excl_words * 32; j0 += kTopkThreads) {
+    const int j = j0 + lane, pos = affix_l + j;
+    const bool drop = j >= L || pos >= T || rs[pos] != shared_slots[j];
+    const unsigned long long bits = __ballot(drop);
+    if (lane == 0) {
+      ex[j0 / 32] = (uint32_t)bits;
+      ex[j0 / 32 + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+  int32_t* out = priv_slots + (size_t)b * stride;
+  uint32_t base = 0;
+  for (int p0 = 0; p0 < T; p0 += kTopkThreads) {
+    const int pos = p0 + tid;
+    int32_t slot = 0;
+    bool keep = false;
+    if (pos < T) {
+      slot = rs[pos];
+      const int j = pos - affix_l;
+      keep = j < 0 || j >= L || slot != shared_slots[j];
+    }
+    uint32_t tot;
+    const uint32_t at = block_exclusive_scan(keep ? 1u : 0u, wave_tot, &tot);
+    if (keep) out[base + at] = slot;
+    base += tot;
+  }
+  // pad the list to whole tiles of `pad` entries with its last slot, so that
+  // tile loads need no bounds (the padded keys are masked by count)
+  const uint32_t padded = (base + pad - 1) / pad * pad;
+  __syncthreads();  // the last entry is written by another thread
+  if (base > 0 && tid < (int)(padded - base)) out[base + tid] = out[base - 1];
+  if (tid == 0) priv_counts[b] = (int32_t)base;
+}
+
+hipError_t launch_shared_plan(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* shared_slots,
+                              int B, int affix_l, int L, int max_kv, int stride, int pad, int32_t* priv_slots,
+                              int32_t* priv_counts, uint32_t* excl, int excl_words, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  if (pad < 1 || pad > kTopkThreads || stride < (max_kv + pad - 1) / pad * pad) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(shared_plan_kernel, dim3(B), dim3(kTopkThreads), 0, st, read_slot, kv_offsets, shared_slots,
+                     affix_l, L, max_kv, stride, pad, priv_slots, priv_counts, excl, excl_words);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void block_slots_kernel(const int32_t* __restrict__ read_slot,
                                                           const int32_t* __restrict__ kv_offsets,
                                                           const int32_t* __restrict__ block_start, int B,

@@ -256,6 +256,41 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
                             acache_stream_t stream);
 
 /*
+ * Read-slot attention of a batch that shares one affix, Section 4.3 and
+ * Appendix C.1 (the shared region is stored once and read by every request,
+ * Section 4.1).  The result is defined exactly as for acache_mapped_attention
+ * with the same q, read_slot and kv_offsets; the extra arguments only say
+ * which slots the requests share, so that the shared region is read once per
+ * group of requests instead of once per request:
+ *   shared_slots [L]  slot of affix key j; position affix_l + j of request b
+ *                     is read from the shared pass when
+ *                     read_slot[kv_offsets[b] + affix_l + j] == shared_slots[j],
+ *                     every other position from its own read slot.
+ * Any read table gives the same result as acache_mapped_attention (up to fp32
+ * summation order); the gain needs most affix positions routed to
+ * shared_slots, as the maps of acache_build_maps / acache_topk_anchors do.
+ * Decode blocks (max_q_per_req <= 32) of bf16 pools with head_dim 128 take
+ * the two-pass path; every other case runs acache_mapped_attention itself.
+ * Requests must satisfy T_b <= max_kv_per_req (positions past it are not
+ * read).  The workspace (size from the query below, given the same pool,
+ * B, n_q, max_q_per_req, n_q_heads, n_layers, max_kv_per_req and L) holds
+ * each request's list of non-shared read slots and its affix exclusion bits
+ * (B * (4 * max_kv_per_req + L / 8) bytes, about); it is rewritten by every
+ * call, so calls that share a workspace must not overlap.
+ */
+int acache_mapped_attention_shared_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t n_q,
+                                                   int32_t max_q_per_req, int32_t n_q_heads, int32_t n_layers,
+                                                   int32_t max_kv_per_req, int32_t L, size_t* bytes /*host*/);
+
+int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets,
+                                   int32_t n_q, int32_t max_q_per_req, const int32_t* read_slot,
+                                   const int32_t* kv_offsets, int32_t max_kv_per_req,
+                                   const int32_t* shared_slots, int32_t affix_l, int32_t L, int32_t B,
+                                   int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   acache_stream_t stream);
+
+/*
  * Host-side check of slot tables (all pointers host).  page_owner[p] is -1
  * for a shared page, b for a page private to request b, -2 for a free page.
  * Checks every slots[i] is in [0, n_pages*page_size) (ERANGE), lies in a page

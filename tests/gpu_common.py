@@ -104,6 +104,12 @@ class Chain:
         self.lse = torch.empty(self.qd.shape[:3], device=DEV)
         A.acache_mapped_attention(self.k, self.v, self.qd, i32(self.q_off), self.read_slot, i32(lay.kv_offsets),
                                   self.out, lse=self.lse, max_q_per_req=self.n_dec, max_kv_per_req=w.T)
+        # the same attention through the shared-affix entry point
+        self.out_sh = torch.empty_like(self.qd)
+        self.lse_sh = torch.empty(self.qd.shape[:3], device=DEV)
+        A.acache_mapped_attention_shared(self.k, self.v, self.qd, i32(self.q_off), self.read_slot,
+                                         i32(lay.kv_offsets), self._keep[1], self.out_sh, lse=self.lse_sh,
+                                         affix_l=w.affix_l, max_q_per_req=self.n_dec, max_kv_per_req=w.T)
         torch.cuda.synchronize()
 
     # ----------------------------------------------------------------- oracle

@@ -142,6 +142,42 @@ def test_scatter_and_attention_validation():
     assert lib.acache_block_slots(None, FAKE, FAKE, 2, 32, FAKE, None) == -1
 
 
+def test_shared_attention_validation_and_workspace():
+    lib = Bd._lib()
+    p = pool()
+    ws = lambda pl, mq, nl=2, L=64, mkv=100: _ws_query(lib, pl, 3, 96, mq, 4, nl, mkv, L)
+    need = ws(p, 32)
+    # private lists, counts, exclusion bits
+    assert need >= 3 * 100 * 4 + 3 * 4 + 3 * 2 * 4
+    assert ws(p, 32, mkv=200) > need and ws(p, 32, L=64000) > need
+    assert ws(p, 33) == 0                        # more than 32 rows per request: single-pass path
+    assert ws(pool(dtype=0, head_dim=64), 32) == 0
+    at = lambda **kw: lib.acache_mapped_attention_shared(
+        ctypes.byref(kw.pop("pool", p)), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE,
+        kw.get("mkv", 100), kw.get("ss", FAKE), kw.get("al", 0), kw.get("L", 64), kw.get("B", 1), kw.get("hq", 4),
+        0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, kw.get("ws", FAKE * 16), kw.get("wsb", 1 << 24),
+        None)
+    assert at(B=0) == 0
+    assert at(hq=5) == -3
+    assert at(mq=9) == -1
+    assert at(scale=-1.0) == -1
+    assert at(out=None) == -1
+    assert at(q=FAKE_MIS) == -9
+    assert at(L=-1) == -1 and at(al=-1) == -1
+    assert at(ss=None) == -1
+    assert at(wsb=16) == -7 and at(ws=None) == -7
+    assert at(ws=FAKE + 4) == -9
+    assert at(B=70000) == -3
+    assert at(B=40000, mkv=60000) == -3          # private lists indexed with 32 bits
+
+
+def _ws_query(lib, pl, B, n_q, mq, hq, nl, mkv, L):
+    out = ctypes.c_size_t()
+    assert lib.acache_mapped_attention_shared_workspace_bytes(ctypes.byref(pl), B, n_q, mq, hq, nl, mkv, L,
+                                                              ctypes.byref(out)) == 0
+    return out.value
+
+
 def test_validate_slots_host_checks():
     ps = 4
     owner = np.array([-1, 0, 0, 1, -2, 1], np.int32)    # page owners: shared, req0, req0, req1, free, req1

@@ -193,6 +193,10 @@ def test_full_size(cid):
         out = torch.empty_like(qd)
         A.acache_mapped_attention(k, v, qd, i32(q_off), read, keep[4], out, max_q_per_req=w.block_len,
                                   max_kv_per_req=w.T)
+        out_sh = torch.empty_like(qd)
+        lse_sh = torch.empty(qd.shape[:3], device=DEV)
+        A.acache_mapped_attention_shared(k, v, qd, i32(q_off), read, keep[4], keep[1], out_sh, lse=lse_sh,
+                                         affix_l=w.affix_l, max_q_per_req=w.block_len, max_kv_per_req=w.T)
         torch.cuda.synchronize()
         r_dst = O.block_slots(r_read, lay.kv_offsets, bstart, w.block_len)
         assert np.array_equal(dst.cpu().numpy(), r_dst)
@@ -207,5 +211,10 @@ def test_full_size(cid):
                                                         [0, w.T], w.n_kv_heads, w.page_size, scale)
                 ok, st = bf16_close(out[n][qsl].float().cpu().numpy(), o_ref)
                 assert ok, f"read-slot attention layer {n} request {b} step {step}: {st}"
-        del qd, bk, bv, out
+                ok, st = bf16_close(out_sh[n][qsl].float().cpu().numpy(), o_ref)
+                assert ok, f"shared-affix read-slot attention layer {n} request {b} step {step}: {st}"
+                # the LSE error follows the fp32 error of the dominant logits, which grows with
+                # their size (heavy-tailed keys): 1e-4 plus 2e-5 of the value
+                np.testing.assert_allclose(lse_sh[n][qsl].cpu().numpy(), l_ref, rtol=2e-5, atol=1e-4)
+        del qd, bk, bv, out, out_sh, lse_sh
     say("done")

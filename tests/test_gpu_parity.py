@@ -51,13 +51,14 @@ def _check_chain(c, layers, fp32):
     kpool, vpool = np_of(c.k), np_of(c.v)
     for i, n in enumerate(c.r_layers):
         assert np.array_equal(kpool[n], c.r_kpool[i]) and np.array_equal(vpool[n], c.r_vpool[i])
-        o = np_of(c.out[n]).astype(np.float64) if fp32 else c.out[n].float().cpu().numpy()
-        if fp32:
-            assert np.abs(o - c.r_out[n]).max() <= 1e-5
-        else:
-            ok, st = bf16_close(o, c.r_out[n])
-            assert ok, f"mapped attention layer {n}: {st}"
-        np.testing.assert_allclose(c.lse[n].cpu().numpy(), c.r_lse[n], atol=1e-4)
+        for tag, out, lse in (("", c.out, c.lse), ("shared-affix ", c.out_sh, c.lse_sh)):
+            o = np_of(out[n]).astype(np.float64) if fp32 else out[n].float().cpu().numpy()
+            if fp32:
+                assert np.abs(o - c.r_out[n]).max() <= 1e-5
+            else:
+                ok, st = bf16_close(o, c.r_out[n])
+                assert ok, f"{tag}mapped attention layer {n}: {st}"
+            np.testing.assert_allclose(lse[n].cpu().numpy(), c.r_lse[n], atol=1e-4)
 
 
 @pytest.mark.parametrize("order,slot_order", [("identity", "page"), ("random", "slot")])
@@ -252,6 +253,88 @@ def test_mapped_attention_ragged(dtype, d):
         lg = lse[n].cpu().numpy()
         assert np.isneginf(lg[~live]).all()
         np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
+
+
+@pytest.mark.parametrize("case", ["mixed", "no-affix", "all-private", "short", "many"])
+def test_shared_affix_attention_seeded(case):
+    """The shared-affix entry point on read tables that route a random part of
+    the affix to the shared slots and the rest anywhere in the pool, with
+    ragged queries (an empty request, a single row, B not a multiple of 4)
+    and contexts (one shorter than the affix end, an empty one).  Its result
+    is defined by the read table alone: same oracle as acache_mapped_attention."""
+    w = Workload(101, "sh", "bf16", 2, 8, 2, 128, (("req", 40), ("affix", 333), ("gen", 64)), 7, 0.2,
+                 page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 5)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=5)
+    nslot = lay.n_pages * w.page_size
+    rng = np.random.default_rng(17)
+    l, L = w.affix_l, w.L
+    shared = lay.shared_slots.astype(np.int32)
+    T = [437, 437, 300, 437, 0, 437, 41]                 # request 2 ends inside the affix, 4 is empty
+    q_counts = [32, 0, 17, 32, 5, 1, 32]
+    if case == "many":
+        q_counts = [32] * 7
+    tables = []
+    for b, t in enumerate(T):
+        rs = rng.integers(0, nslot, t).astype(np.int32)
+        if case != "all-private":
+            j = np.arange(max(0, min(t - l, L)))
+            keep = rng.random(len(j)) < (0.8 if case != "many" else 0.97)
+            rs[l + j[keep]] = shared[j[keep]]
+        tables.append(rs)
+    read = np.concatenate(tables).astype(np.int32)
+    kv_off = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    q_off = np.concatenate([[0], np.cumsum(q_counts)]).astype(np.int32)
+    qd = gen.make_rows(w, int(q_off[-1]), gen.S_QDEC, device=DEV, heads=w.n_q_heads, seed=5)
+    ss = shared if case != "no-affix" else shared[:0]
+    torch.cuda.synchronize()
+    kh, vh, qh = np_of(k), np_of(v), np_of(qd)
+    out = torch.full_like(qd, 7.0)
+    lse = torch.empty(qd.shape[:3], device=DEV)
+    A.acache_mapped_attention_shared(k, v, qd, i32(q_off), i32(read), i32(kv_off), i32(ss), out, lse=lse,
+                                     affix_l=l, max_q_per_req=max(q_counts), max_kv_per_req=max(T))
+    torch.cuda.synchronize()
+    for n in range(w.n_layers):
+        ref, rl = O.mapped_attention_layer(qh[n], kh[n], vh[n], q_off, read, kv_off, w.n_kv_heads, w.page_size,
+                                           1 / math.sqrt(w.head_dim))
+        o = out[n].float().cpu().numpy()
+        live = np.ones(len(o), bool)
+        live[q_off[4]:q_off[5]] = False    # empty context
+        ok, st = bf16_close(o[live], ref[live])
+        assert ok, st
+        assert (o[~live] == 0).all()
+        lg = lse[n].cpu().numpy()
+        assert np.isneginf(lg[~live]).all()
+        np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
+
+
+def test_shared_affix_attention_matches_single_pass_and_repeats():
+    """Two calls in a row (the second with fewer requests) agree with the
+    single-pass entry point on a maps-built decode step."""
+    w = Workload(102, "sh2", "bf16", 2, 8, 8, 128, (("affix", 512), ("req", 24), ("gen", 64)), 9, 0.2,
+                 page_order="random", key_tweak="sinks")
+    c = Chain(w, seed=3)
+    c.run_gpu()
+    for B in (w.batch, 5):
+        q_off = i32(c.q_off[:B + 1])
+        kv_off = i32(c.lay.kv_offsets[:B + 1])
+        n_q = int(c.q_off[B])
+        qd = c.qd[:, :n_q].contiguous()
+        o1 = torch.empty_like(qd)
+        o2 = torch.empty_like(qd)
+        l1 = torch.empty(qd.shape[:3], device=DEV)
+        l2 = torch.empty_like(l1)
+        A.acache_mapped_attention(c.k, c.v, qd, q_off, c.read_slot, kv_off, o1, lse=l1, max_q_per_req=c.n_dec,
+                                  max_kv_per_req=w.T)
+        A.acache_mapped_attention_shared(c.k, c.v, qd, q_off, c.read_slot, kv_off, i32(c.lay.shared_slots), o2,
+                                         lse=l2, affix_l=w.affix_l, max_q_per_req=c.n_dec, max_kv_per_req=w.T)
+        torch.cuda.synchronize()
+        # the two differ in summation order and in the running maxima the bf16
+        # weights are taken against: held to the bar both meet against the oracle
+        ok, st = bf16_close(o2.float().cpu().numpy(), o1.float().cpu().numpy())
+        assert ok, (B, st)
+        assert (l1 - l2).abs().max().item() <= 1e-4
 
 
 def test_identity_map_matches_contiguous_sdpa_on_gpu():
