@@ -570,11 +570,9 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
 //   shared   the affix keys as one tile list for the four requests, loaded
 //            once per workgroup as in attn_rows_mfma; each wave drops the
 //            keys its request does not read from the shared region;
-//   private  each wave streams the rest of its request's read slots through
-//            its own 16 KB of LDS in 32-key tiles, refilling K and V
+//   private  then each wave streams the rest of its request's read slots
+//            through its own 16 KB of LDS in 32-key tiles, refilling K and V
 //            separately so the next tile's loads overlap this tile's math.
-// Workgroups of odd unit index run the phases in the other order, so that
-// co-resident workgroups mix MFMA-bound and memory-bound work.
 __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
   typedef const __attribute__((address_space(4))) int32_t* sc_i32;
@@ -810,15 +808,9 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     }
   };
 
-  if (unit & 1) {
-    private_phase();
-    wg_barrier();  // every wave is done with its private region before the shared tiles land
-    shared_phase();
-  } else {
-    shared_phase();
-    wg_barrier();  // every wave is done with the shared tiles before its private loads land
-    private_phase();
-  }
+  shared_phase();
+  wg_barrier();  // every wave is done with the shared tiles before its private loads land
+  private_phase();
 
   if (!qvalid) return;
   const float lt = lsum + __shfl_xor(lsum, 32, 64);
