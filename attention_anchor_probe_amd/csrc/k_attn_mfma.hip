@@ -106,6 +106,17 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// max / sum of lanes l and l ^ 32 (the two halves of a score column), on the
+// VALU: permlane32_swap leaves lane l's partner value in one of its two results
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous run of logical units so that units sharing K/V (or Q) run on
 // the same XCD and hit its L2.
@@ -426,40 +437,49 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
   const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
   const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
   const uint32_t head_off = (uint32_t)g * p.geo.page_size * ROWB;
-  // the slot table is read-only here: reading it through the constant address
-  // space lets these wave-uniform reads go through scalar loads
-  const __attribute__((address_space(4))) int32_t* table =
-      (const __attribute__((address_space(4))) int32_t*)(p.kv_table + k0);
   const int ntiles = (nk + RB - 1) / RB;
 
-  // this wave loads tile rows 16*wave .. 16*wave+15 of K and of V: DMA
-  // instruction i covers rows 16*wave + 4i + lane/16, one 16-byte chunk per lane
-  int32_t sl[16];
-  auto sload = [&](int tile) {
-    const int kb = tile * RB + 16 * wave;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sl[i] = table[min(kb + i, nk - 1)];
-  };
+  // Tile t's K rows sit in K stage t%2 and its V rows in V stage t%2; this
+  // wave loads rows 16*wave .. 16*wave+15 of each: DMA instruction i covers
+  // rows 16*wave + 4i + lane/16, one 16-byte chunk per lane.  Iteration t
+  // computes the scores of tile t+1 while it takes the softmax and P.V of
+  // tile t (scores computed one iteration earlier), and starts the loads of
+  // K(t+2) and V(t+1): every load has a whole iteration to land.
+  constexpr uint32_t KSTAGE = RB * ROWB;
   // per-lane parts of the DMA addresses: lane/16 picks the row of the 4-row
   // group, lane%16 the LDS chunk; the global chunk is its swizzle
   const int sel = lane >> 4;
+  // slot of the row this lane moves in DMA instruction i of the next K tile
+  // (row 16*wave + 4i + lane/16), loaded a tile ahead of its use
+  const int32_t* vtable = p.kv_table + k0;
+  int32_t vs[4];
+  auto sload = [&](int tile) {
+    const int r0 = tile * RB + 16 * wave + sel;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
+  };
   uint32_t kchunk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
   const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
   const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-  auto dma = [&](int tile) {
-    const uint32_t st = lds0 + (tile % RSTAGES) * RSTAGE_BYTES;
+  // K loads of a tile also record its row offsets (off), which its V loads
+  // reuse one iteration later
+  auto dma_k = [&](int tile, uint32_t* off) {
+    const uint32_t st = lds0 + (tile & 1) * KSTAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // slots are wave-uniform (scalar registers); pick this lane's row's slot
-      const int32_t s0 = sl[4 * i], s1 = sl[4 * i + 1], s2 = sl[4 * i + 2], s3 = sl[4 * i + 3];
-      const int32_t slot = (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
-      const uint32_t off = ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
-                           ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * ROWB;
-      dma16(kbase + off + kchunk[i], st + 4 * i * ROWB);
-      dma16(vbase + off + vchunk, st + RB * ROWB + 4 * i * ROWB);
+      const uint32_t slot = (uint32_t)vs[i];
+      // page index and page bytes are below 2^24, their product below 2^32
+      off[i] = __umul24(slot >> p.geo.page_shift, page_bytes) + head_off +
+               ((slot & (uint32_t)(p.geo.page_size - 1)) << 8);
+      dma16(kbase + off[i] + kchunk[i], st + 4 * i * ROWB);
     }
+  };
+  auto dma_v = [&](int tile, const uint32_t* off) {
+    const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(vbase + off[i] + vchunk, st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
@@ -473,27 +493,22 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
   for (int a = 0; a < 4; ++a) {
     const uint32_t row = 4 * g2 + (i16 >> 2);
     const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-    vrd[a] = RB * ROWB + row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+    vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
   }
 
-  if (ntiles > 0) { sload(0); dma(0); }
-  if (ntiles > 1) sload(1);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this tile's loads have landed
-    wg_barrier();                        // ... in every wave; and every wave is done with the other stage
-    if (tile + 1 < ntiles) {
-      dma(tile + 1);
-      if (tile + 2 < ntiles) sload(tile + 2);
-    }
-    if (!wave_live) continue;
-    const int kb = tile * RB;
-    const char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  auto scores = [&](f32x16* s, int tile) {
+    const char* st = smem + (tile & 1) * KSTAGE;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+  };
+  auto absorb = [&](f32x16* s, int tile) {
+    const int kb = tile * RB;
+    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
     if (kb + RB > nk) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    mr = half_max(mr);
     const float mt = mr * p.c2;
     // rescale only when the running max grows by more than 2^8 (exact either
     // way: O and the row sum carry the same factor)
@@ -528,22 +543,56 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
-          lsum += pv;
+          lsum += pv;  // fp32 weights: the LSE feeds the column mass
           pb[j] = (__bf16)pv;
         }
         // V^T operand: key slots follow the score tile's C layout (keys
         // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const char* vp = st + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
+          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
           o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
         }
       }
+  };
+  // one iteration: sc holds the scores of tile t, sn receives those of t+1;
+  // oc holds the row offsets of tile t+1, on receives those of t+2
+  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
+    wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
+    if (tile + 2 < ntiles) {
+      dma_k(tile + 2, on);
+      if (tile + 3 < ntiles) sload(tile + 3);
+    }
+    if (tile + 1 < ntiles) dma_v(tile + 1, oc);
+    if (!wave_live) return;
+    if (tile + 1 < ntiles) scores(sn, tile + 1);
+    absorb(sc, tile);
+  };
+
+  f32x16 sa[2], sb[2];
+  uint32_t oa[4], ob[4];
+  if (ntiles > 0) {
+    sload(0);
+    dma_k(0, ob);
+    dma_v(0, ob);
+    if (ntiles > 1) {
+      sload(1);
+      dma_k(1, oa);
+      if (ntiles > 2) sload(2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    wg_barrier();
+    if (wave_live) scores(sa, 0);
   }
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    step(tile, sa, sb, oa, ob);
+    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa);
+  }
+  const float lt = half_sum(lsum);
   if (!qvalid) return;
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (p.out) {
     bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
