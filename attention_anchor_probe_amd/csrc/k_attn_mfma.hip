@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
     float mr = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[i]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    mr = half_max(mr);
     const float mt = mr * p.c2;
     // rescale only when the running max grows by more than 2^8 (exact either
     // way: O and the row sum carry the same factor)
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
   float* red = (float*)smem;                      // [wave][a][i][lane]
   float* mw = red + 4 * 4 * 16 * 64;              // [wave][lane]
   float* lw = mw + 4 * 64;                        // [wave][lane]
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float lt = half_sum(lsum);
   __syncthreads();  // every wave is done with the K/V tiles
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -392,6 +392,200 @@ __device__ __forceinline__ uint32_t kswz(uint32_t row, uint32_t chunk) { return 
 __device__ __forceinline__ uint32_t vswz2(uint32_t row, uint32_t chunk) { return chunk ^ ((row & 3u) << 2); }
 }  // namespace
 
+// Key-list source of tile_loop: key j of the list is slot table[j] of the
+// (layer, KV head) whose rows start at kbase / vbase.
+struct TileSrc {
+  const char* kbase;
+  const char* vbase;
+  uint32_t page_bytes;  // bytes of one page of one layer (all KV heads)
+  uint32_t head_off;    // byte offset of the KV head within a page
+  int page_shift;
+  uint32_t page_mask;
+  const int32_t* table;
+  int nk;
+  const uint32_t* excl;  // EXCL only: bit j of excl[j / 32] set drops key j (padded to 64-key tiles)
+};
+
+// Streams a key list through the workgroup's LDS in 64-key tiles into the
+// online softmax (running max m in scaled log2 units, row sum lsum, O
+// accumulators o) of this wave's 32 query rows, whose Q fragments are qf.
+// Every wave of the workgroup calls it: the tile loads are shared, and
+// waves with live == false only help load.
+template <bool EXCL>
+__device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[8],
+                                          bool live, int wave, int lane, float& m, float& lsum, f32x16 (&o)[4]) {
+  const int nk = src.nk;
+  const int ntiles = (nk + RB - 1) / RB;
+  const int g2 = lane >> 5, l32 = lane & 31;
+
+  // Tile t's K rows sit in K stage t%2 and its V rows in V stage t%2; this
+  // wave loads rows 16*wave .. 16*wave+15 of each: DMA instruction i covers
+  // rows 16*wave + 4i + lane/16, one 16-byte chunk per lane.  Iteration t
+  // computes the scores of tile t+1 while it takes the softmax and P.V of
+  // tile t (scores computed one iteration earlier), and starts the loads of
+  // K(t+2) and V(t+1): every load has a whole iteration to land.
+  constexpr uint32_t KSTAGE = RB * ROWB;
+  // per-lane parts of the DMA addresses: lane/16 picks the row of the 4-row
+  // group, lane%16 the LDS chunk; the global chunk is its swizzle
+  const int sel = lane >> 4;
+  // slot of the row this lane moves in DMA instruction i of the next K tile
+  // (row 16*wave + 4i + lane/16), loaded a tile ahead of its use
+  const int32_t* vtable = src.table;
+  int32_t vs[4];
+  auto sload = [&](int tile) {
+    const int r0 = tile * RB + 16 * wave + sel;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
+  };
+  uint32_t kchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
+  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
+  const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
+  // K loads of a tile also record its row offsets (off), which its V loads
+  // reuse one iteration later
+  auto dma_k = [&](int tile, uint32_t* off) {
+    const uint32_t st = lds0 + (tile & 1) * KSTAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t slot = (uint32_t)vs[i];
+      // page index and page bytes are below 2^24, their product below 2^32
+      off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + src.head_off + ((slot & src.page_mask) << 8);
+      dma16(src.kbase + off[i] + kchunk[i], st + 4 * i * ROWB);
+    }
+  };
+  auto dma_v = [&](int tile, const uint32_t* off) {
+    const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(src.vbase + off[i] + vchunk, st + 4 * i * ROWB);
+  };
+
+  // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
+  // sub-block adds compile-time multiples of 16 rows, which keep the swizzle)
+  uint32_t krd[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) krd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
+  const uint32_t i16 = lane & 15;
+  uint32_t vrd[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t row = 4 * g2 + (i16 >> 2);
+    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+    vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+  }
+
+  auto scores = [&](f32x16* s, int tile) {
+    const char* st = smem + (tile & 1) * KSTAGE;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+  };
+  auto absorb = [&](f32x16* s, int tile) {
+    const int kb = tile * RB;
+    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
+    if constexpr (EXCL) {
+      // dropped keys (and the padding past the list) score -inf; lane half
+      // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
+      const __attribute__((address_space(4))) uint32_t* exw =
+          (const __attribute__((address_space(4))) uint32_t*)src.excl;
+      const uint32_t e0 = exw[2 * tile], e1 = exw[2 * tile + 1];
+      if ((e0 | e1) != 0u) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const uint32_t wl = (sub ? e1 : e0) >> (4 * g2);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((wl >> (8 * (i >> 2) + (i & 3))) & 1u) s[sub][i] = -INFINITY;
+        }
+      }
+    } else if (kb + RB > nk) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[sub][i] = -INFINITY;
+    }
+    float mr = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
+    mr = half_max(mr);
+    const float mt = mr * c2;
+    // rescale only when the running max grows by more than 2^8 (exact either
+    // way: O and the row sum carry the same factor)
+    if (mt > m + 8.f) {
+      const float alpha = exp2f(m - mt);
+      lsum *= alpha;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+      m = mt;
+    }
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], c2, nm));
+          lsum += pv;  // fp32 weights: the LSE feeds the column mass
+          pb[j] = (__bf16)pv;
+        }
+        // V^T operand: key slots follow the score tile's C layout (keys
+        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
+        }
+      }
+  };
+  // one iteration: sc holds the scores of tile t, sn receives those of t+1;
+  // oc holds the row offsets of tile t+1, on receives those of t+2
+  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
+    wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
+    if (tile + 2 < ntiles) {
+      dma_k(tile + 2, on);
+      if (tile + 3 < ntiles) sload(tile + 3);
+    }
+    if (tile + 1 < ntiles) dma_v(tile + 1, oc);
+    if (!live) return;
+    if (tile + 1 < ntiles) scores(sn, tile + 1);
+    absorb(sc, tile);
+  };
+
+  f32x16 sa[2], sb[2];
+  uint32_t oa[4], ob[4];
+  if (ntiles > 0) {
+    sload(0);
+    dma_k(0, ob);
+    dma_v(0, ob);
+    if (ntiles > 1) {
+      sload(1);
+      dma_k(1, oa);
+      if (ntiles > 2) sload(2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    wg_barrier();
+    if (live) scores(sa, 0);
+  }
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    step(tile, sa, sb, oa, ob);
+    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa);
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
   __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
   const int unit = xcd_unit(p.per_xcd);
@@ -433,164 +627,17 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) o[a] = f32x16{};
 
-  const char* kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
-  const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
-  const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
-  const uint32_t head_off = (uint32_t)g * p.geo.page_size * ROWB;
-  const int ntiles = (nk + RB - 1) / RB;
-
-  // Tile t's K rows sit in K stage t%2 and its V rows in V stage t%2; this
-  // wave loads rows 16*wave .. 16*wave+15 of each: DMA instruction i covers
-  // rows 16*wave + 4i + lane/16, one 16-byte chunk per lane.  Iteration t
-  // computes the scores of tile t+1 while it takes the softmax and P.V of
-  // tile t (scores computed one iteration earlier), and starts the loads of
-  // K(t+2) and V(t+1): every load has a whole iteration to land.
-  constexpr uint32_t KSTAGE = RB * ROWB;
-  // per-lane parts of the DMA addresses: lane/16 picks the row of the 4-row
-  // group, lane%16 the LDS chunk; the global chunk is its swizzle
-  const int sel = lane >> 4;
-  // slot of the row this lane moves in DMA instruction i of the next K tile
-  // (row 16*wave + 4i + lane/16), loaded a tile ahead of its use
-  const int32_t* vtable = p.kv_table + k0;
-  int32_t vs[4];
-  auto sload = [&](int tile) {
-    const int r0 = tile * RB + 16 * wave + sel;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
-  };
-  uint32_t kchunk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
-  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
-  const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-  // K loads of a tile also record its row offsets (off), which its V loads
-  // reuse one iteration later
-  auto dma_k = [&](int tile, uint32_t* off) {
-    const uint32_t st = lds0 + (tile & 1) * KSTAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t slot = (uint32_t)vs[i];
-      // page index and page bytes are below 2^24, their product below 2^32
-      off[i] = __umul24(slot >> p.geo.page_shift, page_bytes) + head_off +
-               ((slot & (uint32_t)(p.geo.page_size - 1)) << 8);
-      dma16(kbase + off[i] + kchunk[i], st + 4 * i * ROWB);
-    }
-  };
-  auto dma_v = [&](int tile, const uint32_t* off) {
-    const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(vbase + off[i] + vchunk, st + 4 * i * ROWB);
-  };
-
-  // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
-  // sub-block adds compile-time multiples of 16 rows, which keep the swizzle)
-  uint32_t krd[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) krd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
-  const uint32_t i16 = lane & 15;
-  uint32_t vrd[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const uint32_t row = 4 * g2 + (i16 >> 2);
-    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-    vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
-  }
-
-  auto scores = [&](f32x16* s, int tile) {
-    const char* st = smem + (tile & 1) * KSTAGE;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
-  };
-  auto absorb = [&](f32x16* s, int tile) {
-    const int kb = tile * RB;
-    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
-    if (kb + RB > nk) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[sub][i] = -INFINITY;
-    }
-    float mr = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
-    mr = half_max(mr);
-    const float mt = mr * p.c2;
-    // rescale only when the running max grows by more than 2^8 (exact either
-    // way: O and the row sum carry the same factor)
-    if (mt > m + 8.f) {
-      const float alpha = exp2f(m - mt);
-      lsum *= alpha;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
-      m = mt;
-    }
-    const float nm = (m == -INFINITY) ? 0.f : -m;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
-          lsum += pv;  // fp32 weights: the LSE feeds the column mass
-          pb[j] = (__bf16)pv;
-        }
-        // V^T operand: key slots follow the score tile's C layout (keys
-        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
-        }
-      }
-  };
-  // one iteration: sc holds the scores of tile t, sn receives those of t+1;
-  // oc holds the row offsets of tile t+1, on receives those of t+2
-  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on) {
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
-    wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
-    if (tile + 2 < ntiles) {
-      dma_k(tile + 2, on);
-      if (tile + 3 < ntiles) sload(tile + 3);
-    }
-    if (tile + 1 < ntiles) dma_v(tile + 1, oc);
-    if (!wave_live) return;
-    if (tile + 1 < ntiles) scores(sn, tile + 1);
-    absorb(sc, tile);
-  };
-
-  f32x16 sa[2], sb[2];
-  uint32_t oa[4], ob[4];
-  if (ntiles > 0) {
-    sload(0);
-    dma_k(0, ob);
-    dma_v(0, ob);
-    if (ntiles > 1) {
-      sload(1);
-      dma_k(1, oa);
-      if (ntiles > 2) sload(2);
-    }
-    __builtin_amdgcn_s_waitcnt(0x3F70);
-    wg_barrier();
-    if (wave_live) scores(sa, 0);
-  }
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    step(tile, sa, sb, oa, ob);
-    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa);
-  }
+  TileSrc src;
+  src.kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
+  src.vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
+  src.page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+  src.head_off = (uint32_t)g * p.geo.page_size * ROWB;
+  src.page_shift = p.geo.page_shift;
+  src.page_mask = (uint32_t)(p.geo.page_size - 1);
+  src.table = p.kv_table + k0;
+  src.nk = nk;
+  src.excl = nullptr;
+  tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   const float lt = half_sum(lsum);
   if (!qvalid) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -617,8 +664,8 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
 // wave w owns the (at most 32) query rows of request 4t + w.  Two phases feed
 // one online softmax per row:
 //   shared   the affix keys as one tile list for the four requests, loaded
-//            once per workgroup as in attn_rows_mfma; each wave drops the
-//            keys its request does not read from the shared region;
+//            once per workgroup (tile_loop, as in attn_rows_mfma); each wave
+//            drops the keys its request does not read from the shared region;
 //   private  then each wave streams the rest of its request's read slots
 //            through its own 16 KB of LDS in 32-key tiles, refilling K and V
 //            separately so the next tile's loads overlap this tile's math.
@@ -701,7 +748,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     for (int sub = 0; sub < NS; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    mr = half_max(mr);
     const float mt = mr * p.c2;
     if (mt > m + 8.f) {  // lazy rescale, exact either way
       const float alpha = exp2f(m - mt);
@@ -734,73 +781,20 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
       }
   };
 
-  // ---- shared phase: workgroup-wide 64-key tiles of the affix, two stages
+  // ---- shared phase: the affix keys, loaded once for the four requests
   auto shared_phase = [&]() {
-    const int nk = p.n_kv;
-    if (nk <= 0) return;
-    sc_i32 table = (sc_i32)p.kv_table;
-    sc_u32 exw = (sc_u32)(p.excl + (size_t)min(b, p.B - 1) * p.excl_words);
-    const int ntiles = (nk + RB - 1) / RB;
-    int32_t sl[16];
-    uint32_t exn0 = 0, exn1 = 0;
-    auto sload = [&](int tile) {
-      const int kb = tile * RB + 16 * wave;
-      if (kb + 16 <= nk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sl[i] = table[kb + i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sl[i] = table[min(kb + i, nk - 1)];
-      }
-    };
-    auto xload = [&](int tile) {
-      exn0 = exw[2 * tile];
-      exn1 = exw[2 * tile + 1];
-    };
-    const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-    auto dma = [&](int tile) {
-      const uint32_t st = lds0 + (tile % RSTAGES) * RSTAGE_BYTES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off = slot_off(pick(sl[4 * i], sl[4 * i + 1], sl[4 * i + 2], sl[4 * i + 3]));
-        dma16(kbase + off + kchunk[i], st + 4 * i * ROWB);
-        dma16(vbase + off + vchunk, st + RB * ROWB + 4 * i * ROWB);
-      }
-    };
-    sload(0);
-    dma(0);
-    xload(0);
-    if (ntiles > 1) sload(1);
-    for (int tile = 0; tile < ntiles; ++tile) {
-      __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this tile's loads have landed
-      wg_barrier();                        // ... in every wave; and every wave is done with the other stage
-      const uint32_t ex0 = exn0, ex1 = exn1;
-      if (tile + 1 < ntiles) {
-        dma(tile + 1);
-        if (tile + 2 < ntiles) sload(tile + 2);
-        xload(tile + 1);
-      }
-      if (!wave_live) continue;
-      const char* st = smem + (tile % RSTAGES) * RSTAGE_BYTES;
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
-      // dropped keys (and the padding past the affix) score -inf; lane half
-      // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
-      if ((ex0 | ex1) != 0u) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const uint32_t wl = (sub ? ex1 : ex0) >> (4 * g2);
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if ((wl >> (8 * (i >> 2) + (i & 3))) & 1u) s[sub][i] = -INFINITY;
-        }
-      }
-      update(std::integral_constant<int, 2>{}, s, st + RB * ROWB);
-    }
+    if (p.n_kv <= 0) return;
+    TileSrc src;
+    src.kbase = kbase;
+    src.vbase = vbase;
+    src.page_bytes = page_bytes;
+    src.head_off = head_off;
+    src.page_shift = p.geo.page_shift;
+    src.page_mask = (uint32_t)(p.geo.page_size - 1);
+    src.table = p.kv_table;
+    src.nk = p.n_kv;
+    src.excl = p.excl + (size_t)min(b, p.B - 1) * p.excl_words;
+    tile_loop<true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   };
 
   // ---- private phase: this wave's own 32-key tiles, no workgroup barriers
@@ -861,8 +855,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   wg_barrier();  // every wave is done with the shared tiles before its private loads land
   private_phase();
 
+  const float lt = half_sum(lsum);
   if (!qvalid) return;
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const size_t row = ((size_t)n * p.n_q + qrow) * p.n_q_heads + h;
   bf16_t* op = p.out + row * D;
@@ -986,8 +980,8 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
       acc1 += fast_exp2(fmaf(s1[i], p.c2, -lrow[i]));
     }
     if (t1.b != t0.b) {  // last tile of this request: write its partial column masses
-      const float a0 = acc0 + __shfl_xor(acc0, 32, 64);
-      const float a1 = acc1 + __shfl_xor(acc1, 32, 64);
+      const float a0 = half_sum(acc0);
+      const float a1 = half_sum(acc1);
       if (g2 == 0) {
         if (j0 < p.L) part[(size_t)t0.b * p.L + j0] = a0;
         if (j1 < p.L) part[(size_t)t0.b * p.L + j1] = a1;
