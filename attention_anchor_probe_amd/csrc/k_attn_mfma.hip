@@ -381,6 +381,13 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
 }
 
+// The same with a scalar base and a 32-bit per-lane byte offset (saddr form:
+// no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -451,13 +458,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       const uint32_t slot = (uint32_t)vs[i];
       // page index and page bytes are below 2^24, their product below 2^32
       off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + src.head_off + ((slot & src.page_mask) << 8);
-      dma16(src.kbase + off[i] + kchunk[i], st + 4 * i * ROWB);
+      dma16s(src.kbase, off[i] + kchunk[i], st + 4 * i * ROWB);
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src.vbase + off[i] + vchunk, st + 4 * i * ROWB);
+    for (int i = 0; i < 4; ++i) dma16s(src.vbase, off[i] + vchunk, st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
@@ -484,9 +491,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       for (int c = 0; c < 8; ++c)
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
   };
-  auto absorb = [&](f32x16* s, int tile) {
+  // Scores of a tile are masked, and the running max updated (with the lazy
+  // rescale of O and the row sum), as soon as they are computed, at the end
+  // of the iteration before the one that takes their softmax: the body of an
+  // iteration (next scores, this tile's exponentials and P.V) is then free of
+  // branches, so the matrix and vector work of one wave can interleave.
+  auto settle = [&](f32x16* s, int tile) {
     const int kb = tile * RB;
-    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
     if constexpr (EXCL) {
       // dropped keys (and the padding past the list) score -inf; lane half
       // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
@@ -527,6 +538,10 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
         for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
       m = mt;
     }
+  };
+  // exponentials of a settled tile, its row sums and P.V
+  auto absorb = [&](const f32x16* s, int tile) {
+    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
     const float nm = (m == -INFINITY) ? 0.f : -m;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -550,8 +565,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
         }
       }
   };
-  // one iteration: sc holds the scores of tile t, sn receives those of t+1;
-  // oc holds the row offsets of tile t+1, on receives those of t+2
+  // one iteration: sc holds the settled scores of tile t, sn receives those
+  // of t+1; oc holds the row offsets of tile t+1, on receives those of t+2
   auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
     wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
@@ -561,8 +576,11 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     }
     if (tile + 1 < ntiles) dma_v(tile + 1, oc);
     if (!live) return;
-    if (tile + 1 < ntiles) scores(sn, tile + 1);
+    // past the last tile the scores read a stale stage and are never used;
+    // computing them keeps the body branch-free
+    scores(sn, tile + 1);
     absorb(sc, tile);
+    if (tile + 1 < ntiles) settle(sn, tile + 1);
   };
 
   f32x16 sa[2], sb[2];
@@ -578,7 +596,10 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     }
     __builtin_amdgcn_s_waitcnt(0x3F70);
     wg_barrier();
-    if (live) scores(sa, 0);
+    if (live) {
+      scores(sa, 0);
+      settle(sa, 0);
+    }
   }
   for (int tile = 0; tile < ntiles; tile += 2) {
     step(tile, sa, sb, oa, ob);
