@@ -485,10 +485,12 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     const char* st = smem + (tile & 1) * KSTAGE;
     s[0] = f32x16{};
     s[1] = f32x16{};
+    // the two 32-key halves alternate, so that two independent accumulation
+    // chains share the matrix pipe
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int sub = 0; sub < 2; ++sub)
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
   };
   // Scores of a tile are masked, and the running max updated (with the lazy
@@ -543,6 +545,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   auto absorb = [&](const f32x16* s, int tile) {
     const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
     const float nm = (m == -INFINITY) ? 0.f : -m;
+    // fp32 row sums (the LSE feeds the column mass), in four short chains
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -551,7 +555,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], c2, nm));
-          lsum += pv;  // fp32 weights: the LSE feeds the column mass
+          ls[j & 3] += pv;
           pb[j] = (__bf16)pv;
         }
         // V^T operand: key slots follow the score tile's C layout (keys
@@ -564,6 +568,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
           o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
         }
       }
+    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
   // one iteration: sc holds the settled scores of tile t, sn receives those
   // of t+1; oc holds the row offsets of tile t+1, on receives those of t+2
