@@ -277,9 +277,9 @@ def main():
             "traffic_unit": "HBM bytes per launch", "algorithmic_per_launch": wm["probe_flops"],
             "algorithmic_bytes_per_launch": wm["probe_bytes"]}
     mapped_gbs = wm["mapped_bytes"] / t_map / 1e9
-    map_kernels = ("shared_plan_kernel", "attn_rows_mfma<true>", "attn_split_mfma<true>")
+    map_kernels = ("shared_plan_kernel", "attn_shared_mfma")
     map_traffic = [traffic.get(k) for k in map_kernels]
-    roof_mapped = {"kernel": "read-slot attention, shared-affix two-pass call for all layers (" +
+    roof_mapped = {"kernel": "read-slot attention, one shared-affix call for all layers (" +
                              " + ".join(map_kernels) + ")", "bound": "hbm",
                    "achieved": mapped_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": mapped_gbs / PEAK_HBM_GBS,
                    "traffic": sum(map_traffic) if all(t is not None for t in map_traffic) else None,
