@@ -119,6 +119,27 @@ class Setup:
                                          max_kv_per_req=w.T, workspace=self.ws_map)
         ev[6].record()
 
+    def recompute_ms(self, reps):
+        """Recompute-phase read-slot attention (Section 4.3): queries only for
+        every request's recomputed rows (anchors and request positions),
+        keys and values through the read-slot map; timed on its own."""
+        w = self.w
+        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads)
+        orc = torch.empty_like(qr)
+        max_r = int(np.diff(self.lay.rc_offsets).max())
+        rc_off = self._keep[5]
+        run = lambda: A.acache_mapped_attention(self.k, self.v, qr, rc_off, self.read_slot, self.kv_offsets, orc,
+                                                max_q_per_req=max_r, max_kv_per_req=w.T)
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        del qr, orc
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
     def single_pass_ms(self, reps):
         """The same read-slot attention through the single-pass entry point
         (every request streams its whole read list), timed on its own."""
@@ -148,9 +169,10 @@ def work_model(w, K):
     scatter_bytes = 2 * B * R * kv_bytes_per_pos     # read sources, write slots
     nb = B * w.block_len
     mapped_flops = 4.0 * nb * T * d * N * Hq
+    recompute_flops = 4.0 * B * R * T * d * N * Hq
     mapped_bytes = L * kv_bytes_per_pos + B * R * kv_bytes_per_pos + 2 * N * nb * Hq * d * e
     return dict(probe_flops=probe_flops, probe_bytes=probe_bytes, cm_flops=cm_flops, scatter_bytes=scatter_bytes,
-                mapped_flops=mapped_flops, mapped_bytes=mapped_bytes,
+                mapped_flops=mapped_flops, mapped_bytes=mapped_bytes, recompute_flops=recompute_flops,
                 block_bytes=2 * nb * kv_bytes_per_pos)
 
 
@@ -262,6 +284,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     single_ms = S.single_pass_ms(max(3, args.steps // 2))
+    rc_ms = S.recompute_ms(3)
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(Setup.STAGES)}
     wm = work_model(w, S.K)
@@ -295,6 +318,8 @@ def main():
                    "logical_len": w.T, "page_size": w.page_size, "page_order": w.page_order},
         "mapped_attention_pct_bf16_peak": 100.0 * mapped_tflops / PEAK_BF16_TFLOPS,
         "mapped_attention_single_pass_ms": single_ms,
+        "recompute_attention_ms": rc_ms,
+        "recompute_attention_tflops": wm["recompute_flops"] / (rc_ms * 1e-3) / 1e12,
         "probe_ms_per_request": probe_ms_req,
         "probe_attention_tflops": probe_tflops,
         "admission_scatter_gbs": scatter_gbs,

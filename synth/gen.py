@@ -25,7 +25,7 @@ import torch
 from .configs import Workload
 
 # stream ids of the seed tree
-S_PAGES, S_POOL_K, S_POOL_V, S_QPROBE, S_TWEAK, S_SRC_K, S_SRC_V, S_QDEC, S_BLK_K, S_BLK_V, S_SCORES = range(11)
+S_PAGES, S_POOL_K, S_POOL_V, S_QPROBE, S_TWEAK, S_SRC_K, S_SRC_V, S_QDEC, S_BLK_K, S_BLK_V, S_SCORES, S_QRC = range(12)
 
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -163,7 +163,8 @@ def make_probe_q(w: Workload, lay: Layout, device="cpu", seed: int = 0, layers=N
 
 def make_rows(w: Workload, n_rows: int, stream: int, device="cpu", seed: int = 0, layers=None,
               heads=None, step: int = 0):
-    """[n_layers][n_rows][heads][d] of N(0,1): recomputed K/V rows, decode Q."""
+    """[n_layers][n_rows][heads][d] of N(0,1): recomputed K/V rows, decode Q,
+    recompute-phase Q."""
     dt = TORCH_DT[w.dtype]
     layers = range(w.n_layers) if layers is None else layers
     heads = w.n_kv_heads if heads is None else heads

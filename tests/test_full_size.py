@@ -176,6 +176,28 @@ def test_full_size(cid):
         O.scatter(hk[n][None], hv[n][None], hsk[n][None], hsv[n][None], r_rcslot, w.page_size)
         assert np.array_equal(np_of(k[n]), hk[n]) and np.array_equal(np_of(v[n]), hv[n]), f"pool layer {n}"
     del hsk, hsv
+    say("recompute-phase read-slot attention: the recomputed rows of every request over their full read lists")
+    # queries only for the recomputed positions, keys and values through the read-slot map (Section 4.3)
+    max_r = int(np.diff(lay.rc_offsets).max())
+    for n in layers:
+        qr = gen.make_rows(w, n_rc, gen.S_QRC, device=DEV, heads=w.n_q_heads, layers=[n])
+        orc = torch.empty_like(qr)
+        lrc = torch.empty(qr.shape[:3], device=DEV)
+        A.acache_mapped_attention(k, v, qr, keep[5], read, keep[4], orc, lse=lrc, layer_begin=n,
+                                  max_q_per_req=max_r, max_kv_per_req=w.T)
+        torch.cuda.synchronize()
+        hqr = np_of(qr[0])
+        for b in reqs:
+            r0, r1 = int(lay.rc_offsets[b]), int(lay.rc_offsets[b + 1])
+            rows = r0 + np.array(_sampled(r1 - r0, 48, 400 + b + n))
+            o_ref, l_ref = O.mapped_attention_layer(hqr[rows], hk[n], hv[n], [0, len(rows)],
+                                                    r_read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]], [0, w.T],
+                                                    w.n_kv_heads, w.page_size, scale)
+            sel = torch.as_tensor(rows, device=DEV)
+            ok, st = bf16_close(orc[0][sel].float().cpu().numpy(), o_ref)
+            assert ok, f"recompute-phase attention layer {n} request {b}: {st}"
+            np.testing.assert_allclose(lrc[0][sel].cpu().numpy(), l_ref, rtol=2e-5, atol=1e-4)
+        del qr, orc, lrc
     q_off = np.arange(w.batch + 1) * w.block_len
     for step in range(w.steps):
         say(f"decode step {step}: block slots, block store, read-slot attention (all layers)")
