@@ -225,3 +225,43 @@ def block_slots(read_slot, kv_offsets, block_start, block_len):
         for i in range(block_len):
             out.append(int(read_slot[kv_offsets[b] + block_start[b] + i]))
     return np.array(out, np.int64)
+
+
+# ----------------------------------------------------------------------------
+# DropNA ablation (Section 5.3, Figure 5): same Anchor Tokens, the non-anchor
+# affix cache discarded
+# ----------------------------------------------------------------------------
+def dropna_read_table(read_slot_b, anchors_b, affix_l, L):
+    """Read list of one request under DropNA: its KeepNA read-slot list with
+    every non-anchor affix position (p in F \\ A) left out, in logical
+    order.  Anchors and all positions outside the affix keep their slots."""
+    anchor_set = set(int(a) for a in anchors_b)
+    keep = []
+    for p in range(len(read_slot_b)):
+        in_affix = affix_l <= p < affix_l + L
+        if in_affix and p not in anchor_set:
+            continue
+        keep.append(int(read_slot_b[p]))
+    return np.array(keep, np.int64)
+
+
+# ----------------------------------------------------------------------------
+# KV-cache footprint of the two layouts (Section 4.1 shared/private regions,
+# Appendix B.2: blocks are allocated per region at block granularity)
+# ----------------------------------------------------------------------------
+def kv_footprint(seq_len, L, K, page_size, slot_bytes):
+    """Peak KV bytes with every request of the batch resident.
+
+    dense:   each request holds its whole logical context in its own pages
+             (the baseline cache, no sharing);
+    shared:  the affix is stored once, in ceil(L / ps) shared pages;
+    private: each request holds its recompute set R_b = K + (T_b - L)
+             (anchors and request positions) in ceil(R_b / ps) pages;
+    dropna:  the private pages alone (the non-anchor affix cache dropped).
+    slot_bytes = K and V bytes of one slot over all layers and KV heads."""
+    pages = lambda n: -(-int(n) // page_size)
+    dense = sum(pages(t) for t in seq_len) * page_size * slot_bytes
+    shared = pages(L) * page_size * slot_bytes if len(seq_len) else 0
+    private = sum(pages(K + t - L) for t in seq_len) * page_size * slot_bytes
+    return {"dense": dense, "shared": shared, "private": private, "acache": shared + private,
+            "dropna": private}

@@ -509,3 +509,87 @@ def test_empty_context_is_empty_sum():
     o2, _ = O.mapped_attention_layer(qd[0][2:], k[0], v[0], [0, 2], read, [0, 5], w.n_kv_heads, w.page_size,
                                      1 / math.sqrt(w.head_dim))
     assert np.array_equal(o[2:], o2)
+
+
+# ---------------------------------------------------------------------------
+# DropNA (Section 5.3, Figure 5) and the KV footprint (Section 4.1, App. B.2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rate", [0.0, 0.3, 1.0])
+def test_dropna_table_and_attention(rate):
+    """DropNA keeps the same anchors and drops the non-anchor affix cache: its
+    read list is the KeepNA list minus F \\ A (T - L + K entries), it equals
+    the KeepNA list at ratio 1 (no non-anchor tokens remain), and attention
+    over it equals attention over the full logical context with the dropped
+    positions masked out (torch SDPA with a boolean mask, fp64)."""
+    w = tiny_workload(rate=rate)
+    K, lay, k, v, q = build_case(w)
+    scale = 1 / math.sqrt(w.head_dim)
+    s = O.probe_scores(q, k, v, lay.shared_slots, w.page_size, w.n_kv_heads, lay.masked_rows,
+                       lay.masked_offsets, scale)
+    anchors = [O.topk_anchors(s[b], K, w.affix_l) for b in range(w.batch)]
+    read, rcp, rcs = full_maps(w, K, lay, anchors)
+    n_rows = len(rcs)
+    sk = np_of(gen.make_rows(w, n_rows, gen.S_SRC_K))
+    sv = np_of(gen.make_rows(w, n_rows, gen.S_SRC_V))
+    kp, vp = k.copy(), v.copy()
+    O.scatter(kp, vp, sk, sv, rcs, w.page_size)
+    qd = np_of(gen.make_rows(w, 2 * w.batch, gen.S_QDEC, heads=w.n_q_heads))
+    for b in range(w.batch):
+        T = int(lay.seq_len[b])
+        rb = read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]]
+        dn = O.dropna_read_table(rb, anchors[b], w.affix_l, w.L)
+        assert len(dn) == T - w.L + K
+        if rate == 1.0:
+            assert dn.tolist() == rb.tolist()
+        for n in range(w.n_layers):
+            om, _ = O.mapped_attention_layer(qd[n, 2 * b:2 * b + 2], kp[n], vp[n], [0, 2], dn, [0, len(dn)],
+                                             w.n_kv_heads, w.page_size, scale)
+            fresh_pos = set(int(a) for a in anchors[b])
+            r0, r1 = lay.rc_offsets[b], lay.rc_offsets[b + 1]
+            Kl = torch.from_numpy(_logical_kv(w, lay, k[n], sk[n, r0:r1], fresh_pos))
+            Vl = torch.from_numpy(_logical_kv(w, lay, v[n], sv[n, r0:r1], fresh_pos))
+            keep = torch.tensor([not (w.affix_l <= p < w.affix_l + w.L) or p in fresh_pos for p in range(T)])
+            qq = torch.from_numpy(O.decode(qd[n, 2 * b:2 * b + 2]))       # [2][Hq][d]
+            g = w.n_q_heads // w.n_kv_heads
+            Kh = Kl.permute(1, 0, 2).repeat_interleave(g, 0)                 # [Hq][T][d]
+            Vh = Vl.permute(1, 0, 2).repeat_interleave(g, 0)
+            ref = torch.nn.functional.scaled_dot_product_attention(qq.permute(1, 0, 2), Kh, Vh, attn_mask=keep)
+            np.testing.assert_allclose(om, ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_kv_footprint_closed_form_and_layout_count():
+    """The footprint counts the pages a layout actually holds: the distinct
+    pages of the shared slots plus each request's private pages (counted from
+    the tables built for it), and the dense baseline's whole-context pages."""
+    for segments, rate, B in [((("affix", 37), ("req", 5), ("gen", 9)), 0.3, 3),
+                              ((("req", 6), ("affix", 64), ("gen", 16)), 0.2, 5),
+                              ((("req", 2), ("gen", 7), ("affix", 20)), 1.0, 2)]:
+        w = tiny_workload(segments=segments, rate=rate, batch=B)
+        K = O.anchor_count(w.L, w.rate)
+        lay = gen.make_layout(w, K, 3)
+        anchors = [np.arange(w.affix_l, w.affix_l + K)] * B
+        read, rcp, rcs = full_maps(w, K, lay, anchors)
+        slot_bytes = 7
+        f = O.kv_footprint(lay.seq_len.tolist(), w.L, K, w.page_size, slot_bytes)
+        pages = lambda slots: len(set(int(x) // w.page_size for x in slots))
+        assert f["shared"] == pages(lay.shared_slots) * w.page_size * slot_bytes
+        priv = sum(pages(rcs[lay.rc_offsets[b]:lay.rc_offsets[b + 1]]) for b in range(B))
+        assert f["private"] == priv * w.page_size * slot_bytes
+        assert f["dense"] == sum(-(-int(t) // w.page_size) for t in lay.seq_len) * w.page_size * slot_bytes
+        assert f["acache"] == f["shared"] + f["private"] and f["dropna"] == f["private"]
+
+
+def test_kv_footprint_hand_numbers_and_trend():
+    """LLaDA-8B shapes (32 layers, 32 KV heads, d=128, bf16: 512 KiB of K and V
+    per slot), 16-slot pages, affix 4096, 512 request positions, K = 820:
+    dense 16 * 288 pages, ACache 256 + 16 * 84 pages.  Appendix B.2: at batch
+    1 the separate shared and private blocks cost at least the dense cache,
+    and the saving grows with the batch."""
+    sb = 32 * 32 * 128 * 2 * 2
+    f = O.kv_footprint([4608] * 16, 4096, 820, 16, sb)
+    assert f["dense"] == 16 * 288 * 16 * sb == 38654705664
+    assert f["acache"] == (256 + 16 * 84) * 16 * sb == 13421772800
+    one = O.kv_footprint([4608], 4096, 820, 16, sb)
+    assert one["acache"] >= one["dense"]
+    red = [1 - O.kv_footprint([4608] * B, 4096, 820, 16, sb)["acache"] / (B * 288 * 16 * sb) for B in (1, 2, 4, 16)]
+    assert red == sorted(red) and red[-1] > 0.6
