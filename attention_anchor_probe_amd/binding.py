@@ -68,6 +68,8 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                         _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_kv_footprint": ([_I, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64),
+                             ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "acache_validate_slots": ([_P, _I, _P, _P, _I, _I, _I, ctypes.POINTER(_I)], ctypes.c_int),
 }
 EXPORTS = tuple(_SIG)
@@ -306,6 +308,19 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention_shared", st)
+
+
+def acache_kv_footprint(seq_len, L, K, page_size, n_layers, n_kv_heads, head_dim, dtype="bf16"):
+    """Bytes of the shared region, of all private regions and of a dense
+    per-request cache (host arithmetic; seq_len is a host sequence)."""
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(seq_len), dtype=np.int32)
+    out = [ctypes.c_uint64() for _ in range(3)]
+    dt = {"f32": 0, "bf16": 1}[dtype] if isinstance(dtype, str) else int(dtype)
+    _check("acache_kv_footprint", _lib().acache_kv_footprint(
+        len(sl), sl.ctypes.data_as(ctypes.c_void_p) if len(sl) else None, int(L), int(K), int(page_size),
+        int(n_layers), int(n_kv_heads), int(head_dim), dt, *(ctypes.byref(x) for x in out)))
+    return {"shared": out[0].value, "private": out[1].value, "dense": out[2].value}
 
 
 def acache_validate_slots(slots, page_owner, n_pages, page_size, owner=None, distinct=True):

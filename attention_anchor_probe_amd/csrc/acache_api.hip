@@ -459,6 +459,29 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
+int acache_kv_footprint(int32_t B, const int32_t* seq_len, int32_t L, int32_t K, int32_t page_size,
+                        int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                        uint64_t* shared_bytes, uint64_t* private_bytes, uint64_t* dense_bytes) {
+  if (!shared_bytes || !private_bytes || !dense_bytes) return ACACHE_EINVAL;
+  if (B < 0 || L < 0 || K < 0 || K > L || page_size <= 0 || n_layers < 0 || n_kv_heads < 0 || head_dim < 0)
+    return ACACHE_EINVAL;
+  if (dtype != ACACHE_F32 && dtype != ACACHE_BF16) return ACACHE_EDTYPE;
+  if (B > 0 && !seq_len) return ACACHE_EINVAL;
+  const uint64_t page = (uint64_t)page_size * (uint64_t)n_layers * (uint64_t)n_kv_heads * (uint64_t)head_dim * 2u *
+                        (uint64_t)elem_bytes(dtype);
+  auto pages = [&](int64_t n) -> uint64_t { return (uint64_t)((n + page_size - 1) / page_size); };
+  uint64_t priv = 0, dense = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_len[b] < L) return ACACHE_EINVAL;
+    priv += pages((int64_t)K + seq_len[b] - L);
+    dense += pages(seq_len[b]);
+  }
+  *shared_bytes = B > 0 ? pages(L) * page : 0;
+  *private_bytes = priv * page;
+  *dense_bytes = dense * page;
+  return ACACHE_OK;
+}
+
 int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner, const int32_t* page_owner,
                           int32_t n_pages, int32_t page_size, int32_t distinct, int32_t* bad_index) {
   if (n < 0 || n_pages <= 0 || page_size <= 0 || (page_size & (page_size - 1))) return ACACHE_EINVAL;

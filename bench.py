@@ -140,6 +140,23 @@ class Setup:
         del qr, orc
         return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
+    def dropna_ms(self, reps):
+        """Decode-block attention under the DropNA ablation (Section 5.3): the
+        same queries over the recompute map only (the non-anchor affix cache
+        dropped); timed on its own."""
+        w = self.w
+        max_r = int(np.diff(self.lay.rc_offsets).max())
+        run = lambda: A.acache_mapped_attention(self.k, self.v, self.qd, self.q_off, self.rc_slot, self._keep[5],
+                                                self.out, max_q_per_req=w.block_len, max_kv_per_req=max_r)
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
     def single_pass_ms(self, reps):
         """The same read-slot attention through the single-pass entry point
         (every request streams its whole read list), timed on its own."""
@@ -285,6 +302,8 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     single_ms = S.single_pass_ms(max(3, args.steps // 2))
     rc_ms = S.recompute_ms(3)
+    dropna_ms = S.dropna_ms(max(3, args.steps // 2))
+    fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(Setup.STAGES)}
     wm = work_model(w, S.K)
@@ -319,6 +338,10 @@ def main():
         "mapped_attention_pct_bf16_peak": 100.0 * mapped_tflops / PEAK_BF16_TFLOPS,
         "mapped_attention_single_pass_ms": single_ms,
         "recompute_attention_ms": rc_ms,
+        "dropna_mapped_attention_ms": dropna_ms,
+        "kv_footprint_gb": {"shared": fp["shared"] / 1e9, "private": fp["private"] / 1e9,
+                            "dense": fp["dense"] / 1e9,
+                            "acache_saving": 1 - (fp["shared"] + fp["private"]) / fp["dense"]},
         "recompute_attention_tflops": wm["recompute_flops"] / (rc_ms * 1e-3) / 1e12,
         "probe_ms_per_request": probe_ms_req,
         "probe_attention_tflops": probe_tflops,

@@ -177,6 +177,10 @@ int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t 
  *   recompute_slot[rc_offsets[b] + i] = its private slot (the write-side map).
  * kv_offsets[b+1]-kv_offsets[b] must equal T_b and rc_offsets[b+1]-rc_offsets[b]
  * must equal K + T_b - L; request b needs ceil((K + T_b - L)/page_size) pages.
+ * recompute_slot with rc_offsets is also the DropNA read table (Section 5.3,
+ * Figure 5: the same anchors with the non-anchor affix cache discarded):
+ * acache_mapped_attention over (recompute_slot, rc_offsets) is the DropNA
+ * attention.
  */
 typedef struct acache_map_args {
   int32_t B;
@@ -289,6 +293,26 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                    int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
                                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                                    acache_stream_t stream);
+
+/*
+ * KV-cache footprint with every request resident (host arithmetic; all
+ * pointers host).  Section 4.1: one shared region holds the affix once and
+ * each request's private region holds its recompute set R_b (anchors and
+ * request positions, K + seq_len[b] - L slots); Appendix B.2: the regions
+ * are allocated at block (page) granularity.  In pages:
+ *   shared  = ceil(L / page_size)                     (0 when B = 0),
+ *   private = sum_b ceil((K + seq_len[b] - L) / page_size),
+ *   dense   = sum_b ceil(seq_len[b] / page_size)      (no sharing: every
+ *             request holds its whole context, the baseline cache);
+ * each page is page_size * n_layers * n_kv_heads * head_dim * 2 (K and V)
+ * elements of `dtype`.  The DropNA cache is the private pages alone.
+ * EINVAL for a NULL output or seq_len (with B > 0), negative sizes,
+ * K > L or seq_len[b] < L; EDTYPE for an unknown dtype.
+ */
+int acache_kv_footprint(int32_t B, const int32_t* seq_len /*host*/, int32_t L, int32_t K,
+                        int32_t page_size, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t dtype, uint64_t* shared_bytes, uint64_t* private_bytes,
+                        uint64_t* dense_bytes);
 
 /*
  * Host-side check of slot tables (all pointers host).  page_owner[p] is -1

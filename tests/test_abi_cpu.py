@@ -194,3 +194,27 @@ def test_validate_slots_host_checks():
                                    owner=np.array([0, 1], np.int32)) == (0, -1)
     assert A.acache_validate_slots(np.array([4, 5], np.int32), owner, 6, ps,
                                    owner=np.array([0, 1], np.int32)) == (-5, 1)
+
+
+def test_kv_footprint_matches_oracle():
+    from oracle import acache_oracle as O
+    from synth.configs import WORKLOADS
+    for w in WORKLOADS.values():
+        K = A.acache_anchor_count(w.L, w.rate)
+        seq = [w.T] * w.batch
+        got = A.acache_kv_footprint(seq, w.L, K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
+        sb = w.n_layers * w.n_kv_heads * w.head_dim * 2 * (4 if w.dtype == "f32" else 2)
+        ref = O.kv_footprint(seq, w.L, K, w.page_size, sb)
+        assert got == {"shared": ref["shared"], "private": ref["private"], "dense": ref["dense"]}, w.name
+    ragged = [70, 65, 99]
+    got = A.acache_kv_footprint(ragged, 64, 13, 16, 2, 3, 8, "f32")
+    assert got == {k: v for k, v in O.kv_footprint(ragged, 64, 13, 16, 2 * 3 * 8 * 2 * 4).items()
+                   if k in ("shared", "private", "dense")}
+    assert A.acache_kv_footprint([], 64, 13, 16, 2, 3, 8) == {"shared": 0, "private": 0, "dense": 0}
+    for bad in (dict(seq_len=[10], L=64), dict(K=70), dict(page_size=0)):
+        a = dict(seq_len=[100], L=64, K=13, page_size=16)
+        a.update(bad)
+        with pytest.raises(A.AcacheError):
+            A.acache_kv_footprint(a["seq_len"], a["L"], a["K"], a["page_size"], 2, 3, 8)
+    with pytest.raises(A.AcacheError):
+        A.acache_kv_footprint([100], 64, 13, 16, 2, 3, 8, 7)

@@ -410,3 +410,34 @@ def test_probe_is_deterministic_and_accumulates():
                               i32(lay.shared_slots), s3, max_masked=w.m, layer_begin=n)
     torch.cuda.synchronize()
     np.testing.assert_allclose(s3.cpu().numpy(), s1.cpu().numpy(), rtol=1e-5)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_dropna_attention(idx):
+    """DropNA (Section 5.3): the recompute map doubles as the read table with
+    the non-anchor affix cache dropped.  The library's recompute slots equal
+    the oracle's DropNA tables bit for bit, and the read-slot attention over
+    them matches the oracle's attention over those tables."""
+    name, w = SMALL[idx]
+    c = Chain(w, n_dec=min(w.block_len, w.m), seed=7)
+    c.run_gpu()
+    c.run_oracle()
+    an = c.anchors.cpu().numpy()
+    if any(an[b].tolist() != c.r_anchors[b].tolist() for b in range(w.batch)):
+        pytest.skip("anchor sets agree only within the tie band")
+    lay = c.lay
+    dn = [O.dropna_read_table(c.r_read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]], c.r_anchors[b], w.affix_l, w.L)
+          for b in range(w.batch)]
+    assert np.array_equal(c.rc_slot.cpu().numpy(), np.concatenate(dn))
+    out = torch.empty_like(c.qd)
+    lse = torch.empty(c.qd.shape[:3], device=DEV)
+    A.acache_mapped_attention(c.k, c.v, c.qd, i32(c.q_off), c.rc_slot, i32(lay.rc_offsets), out, lse=lse,
+                              max_q_per_req=c.n_dec, max_kv_per_req=int(np.diff(lay.rc_offsets).max()))
+    torch.cuda.synchronize()
+    dn_off = np.concatenate([[0], np.cumsum([len(x) for x in dn])])
+    for i, n in enumerate(c.r_layers):
+        ref, rl = O.mapped_attention_layer(c.h["qd"][n], c.r_kpool[i], c.r_vpool[i], c.q_off, np.concatenate(dn),
+                                           dn_off, w.n_kv_heads, w.page_size, c.scale)
+        ok, st = bf16_close(out[n].float().cpu().numpy(), ref)
+        assert ok, f"DropNA attention layer {n}: {st}"
+        np.testing.assert_allclose(lse[n].cpu().numpy(), rl, atol=1e-4)
