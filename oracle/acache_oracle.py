@@ -265,3 +265,52 @@ def kv_footprint(seq_len, L, K, page_size, slot_bytes):
     private = sum(pages(K + t - L) for t in seq_len) * page_size * slot_bytes
     return {"dense": dense, "shared": shared, "private": private, "acache": shared + private,
             "dropna": private}
+
+
+# ----------------------------------------------------------------------------
+# Full-context reading of the probe normaliser (the alternative to Eq. (4)
+# read literally): each non-affix row's softmax runs over the affix keys AND
+# the request's own non-affix keys; the scores still sum only affix weights
+# ----------------------------------------------------------------------------
+def probe_layer_full(q_layer, k_layer, v_layer, shared_slots, row_offsets, na_slots, na_offsets,
+                     page_size, n_kv_heads, masked_rows, masked_offsets, scale):
+    """One layer of the probe with the full-context normaliser.
+
+    Request b's non-affix rows are q rows row_offsets[b]..row_offsets[b+1];
+    its non-affix keys and values sit at slots na_slots[na_offsets[b] ..
+    na_offsets[b+1]].  Each row attends over [affix keys, own non-affix keys]
+    in one softmax.  Returns O [rows][Hq][d], LSE [rows][Hq] (natural log)
+    and the layer's [B][L] sum of the affix weights over heads and the masked
+    rows of each request (masked_rows index the batch's rows)."""
+    rows, Hq, d = q_layer.shape
+    L = len(shared_slots)
+    B = len(row_offsets) - 1
+    o = np.zeros((rows, Hq, d))
+    lse = np.zeros((rows, Hq))
+    s = np.zeros((B, L))
+    for b in range(B):
+        r0, r1 = row_offsets[b], row_offsets[b + 1]
+        own = na_slots[na_offsets[b]:na_offsets[b + 1]]
+        mk = masked_rows[masked_offsets[b]:masked_offsets[b + 1]] - r0     # masked rows of b, local index
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, n_kv_heads)
+            Kc = np.concatenate([slot_rows(k_layer, shared_slots, g, page_size),
+                                 slot_rows(k_layer, own, g, page_size)])
+            Vc = np.concatenate([slot_rows(v_layer, shared_slots, g, page_size),
+                                 slot_rows(v_layer, own, g, page_size)])
+            Q = decode(q_layer[r0:r1, h, :])
+            A, lse[r0:r1, h] = softmax_rows((Q @ Kc.T) * scale)
+            o[r0:r1, h, :] = A @ Vc
+            s[b] += A[mk, :L].sum(axis=0)
+    return o, lse, s
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets from the attentions
+    over each (their outputs and natural-log log-sum-exps): the softmax over
+    the union weights each part by its share of the total exponential mass.
+    Two empty parts give O = 0 and LSE = -inf."""
+    lse = np.logaddexp(lse_a, lse_b)
+    wa = np.where(np.isneginf(lse), 0.0, np.exp(lse_a - np.where(np.isneginf(lse), 0.0, lse)))
+    wb = np.where(np.isneginf(lse), 0.0, np.exp(lse_b - np.where(np.isneginf(lse), 0.0, lse)))
+    return wa[..., None] * o_a + wb[..., None] * o_b, lse

@@ -593,3 +593,69 @@ def test_kv_footprint_hand_numbers_and_trend():
     assert one["acache"] >= one["dense"]
     red = [1 - O.kv_footprint([4608] * B, 4096, 820, 16, sb)["acache"] / (B * 288 * 16 * sb) for B in (1, 2, 4, 16)]
     assert red == sorted(red) and red[-1] > 0.6
+
+
+# ---------------------------------------------------------------------------
+# full-context normaliser of the probe (the alternative reading of Eq. (4))
+# ---------------------------------------------------------------------------
+def _na_slots(w, lay):
+    """Slots for each request's non-affix keys: the first P_b slots of its
+    private pages (any valid slots serve; the pool is random there)."""
+    out, offs = [], [0]
+    for b in range(w.batch):
+        pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+        P_b = int(lay.row_offsets[b + 1] - lay.row_offsets[b])
+        out += [int(pp[i // w.page_size]) * w.page_size + i % w.page_size for i in range(P_b)]
+        offs.append(len(out))
+    return np.array(out, np.int64), np.array(offs, np.int64)
+
+
+def test_probe_full_normaliser_pins():
+    """(i) O and LSE equal torch SDPA / logsumexp over [affix keys, own
+    non-affix keys] (fp64); (ii) the affix weights under the full normaliser
+    are the affix-only weights times exp(LSE_aff - LSE_all), summed over the
+    masked rows; (iii) merging the affix-only attention with the attention
+    over the own keys gives the same O and LSE; (iv) with no own keys the
+    full normaliser is the affix-only one."""
+    w = tiny_workload(segments=(("req", 3), ("affix", 11), ("req", 2), ("gen", 5)), batch=2)
+    K, lay, k, v, q = build_case(w)
+    scale = 1 / math.sqrt(w.head_dim)
+    na, na_off = _na_slots(w, lay)
+    for n in range(w.n_layers):
+        of, lf, sf = O.probe_layer_full(q[n], k[n], v[n], lay.shared_slots, lay.row_offsets, na, na_off, w.page_size,
+                                        w.n_kv_heads, lay.masked_rows, lay.masked_offsets, scale)
+        oa, la, _ = O.probe_layer(q[n], k[n], v[n], lay.shared_slots, w.page_size, w.n_kv_heads, lay.masked_rows,
+                                  lay.masked_offsets, scale)
+        on, ln = O.mapped_attention_layer(q[n], k[n], v[n], lay.row_offsets, na, na_off, w.n_kv_heads, w.page_size,
+                                          scale)
+        om, lm = O.lse_merge(oa, la, on, ln)
+        np.testing.assert_allclose(om, of, atol=1e-12)
+        np.testing.assert_allclose(lm, lf, atol=1e-12)
+        sref = np.zeros_like(sf)
+        for b in range(w.batch):
+            r0, r1 = lay.row_offsets[b], lay.row_offsets[b + 1]
+            own = na[na_off[b]:na_off[b + 1]]
+            for h in range(w.n_q_heads):
+                g = h // (w.n_q_heads // w.n_kv_heads)
+                kk = torch.from_numpy(np.concatenate([O.slot_rows(k[n], lay.shared_slots, g, w.page_size),
+                                                      O.slot_rows(k[n], own, g, w.page_size)]))
+                vv = torch.from_numpy(np.concatenate([O.slot_rows(v[n], lay.shared_slots, g, w.page_size),
+                                                      O.slot_rows(v[n], own, g, w.page_size)]))
+                qq = torch.from_numpy(O.decode(q[n, r0:r1, h, :]))
+                ref = torch.nn.functional.scaled_dot_product_attention(qq[None], kk[None], vv[None])[0]
+                np.testing.assert_allclose(of[r0:r1, h], ref.numpy(), atol=1e-12)
+                lall = torch.logsumexp((qq @ kk.T) * scale, dim=1).numpy()
+                np.testing.assert_allclose(lf[r0:r1, h], lall, atol=1e-12)
+                aff = torch.softmax((qq @ kk[:w.L].T) * scale, dim=1).numpy()        # affix-only weights
+                mk = lay.masked_rows[lay.masked_offsets[b]:lay.masked_offsets[b + 1]] - r0
+                sref[b] += (aff[mk] * np.exp(la[r0:r1, h][mk] - lall[mk])[:, None]).sum(axis=0)
+        np.testing.assert_allclose(sf, sref, rtol=1e-10, atol=1e-14)
+        assert (sf.sum(axis=1) < w.n_q_heads * np.diff(lay.masked_offsets)).all()
+        o0, l0, s0 = O.probe_layer_full(q[n], k[n], v[n], lay.shared_slots, lay.row_offsets, na[:0],
+                                        np.zeros(w.batch + 1, np.int64), w.page_size, w.n_kv_heads,
+                                        lay.masked_rows, lay.masked_offsets, scale)
+        _, _, sa = O.probe_layer(q[n], k[n], v[n], lay.shared_slots, w.page_size, w.n_kv_heads, lay.masked_rows,
+                                 lay.masked_offsets, scale)
+        np.testing.assert_allclose(o0, oa, atol=1e-12)
+        np.testing.assert_allclose(l0, la, atol=1e-12)
+        np.testing.assert_allclose(s0, sa, atol=1e-12)
