@@ -68,6 +68,7 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                         _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_lse_merge": ([_I, ctypes.c_int64, _I, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "acache_kv_footprint": ([_I, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64),
                              ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "acache_validate_slots": ([_P, _I, _P, _P, _I, _I, _I, ctypes.POINTER(_I)], ctypes.c_int),
@@ -308,6 +309,22 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention_shared", st)
+
+
+def acache_lse_merge(lse_a, lse_b, lse, o_a=None, o_b=None, o=None, stream=None):
+    """Merge two attentions over disjoint key sets.  lse_*: fp32 [..., H];
+    o_*: [..., H, d] (all given or none)."""
+    if o is not None:
+        d = o.shape[-1]
+        dt = o.dtype
+        if o_a is None or o_b is None or o_a.dtype != dt or o_b.dtype != dt:
+            raise ValueError("o_a, o_b and o must be given together with one dtype")
+    else:
+        d, dt = 16, torch.float32
+    st = _lib().acache_lse_merge(_DT[dt], int(lse.numel()), int(d), _dev(o_a), _dev(lse_a, torch.float32),
+                                 _dev(o_b), _dev(lse_b, torch.float32), _dev(o), _dev(lse, torch.float32),
+                                 _stream(stream))
+    _check("acache_lse_merge", st)
 
 
 def acache_kv_footprint(seq_len, L, K, page_size, n_layers, n_kv_heads, head_dim, dtype="bf16"):

@@ -459,6 +459,17 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
+int acache_lse_merge(int32_t dtype, int64_t n_pairs, int32_t head_dim, const void* o_a, const float* lse_a,
+                     const void* o_b, const float* lse_b, void* o, float* lse, acache_stream_t stream) {
+  if (dtype != ACACHE_F32 && dtype != ACACHE_BF16) return ACACHE_EDTYPE;
+  if (n_pairs < 0 || !lse_a || !lse_b || !lse) return ACACHE_EINVAL;
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128) return ACACHE_ESHAPE;
+  const int n_o = (o_a != nullptr) + (o_b != nullptr) + (o != nullptr);
+  if (n_o != 0 && n_o != 3) return ACACHE_EINVAL;
+  if (n_o == 3 && (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o))) return ACACHE_EALIGN;
+  return status_of(launch_lse_merge(dtype, n_pairs, head_dim, o_a, lse_a, o_b, lse_b, o, lse, (hipStream_t)stream));
+}
+
 int acache_kv_footprint(int32_t B, const int32_t* seq_len, int32_t L, int32_t K, int32_t page_size,
                         int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
                         uint64_t* shared_bytes, uint64_t* private_bytes, uint64_t* dense_bytes) {

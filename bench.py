@@ -157,6 +157,43 @@ class Setup:
         torch.cuda.synchronize()
         return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
+    def full_normaliser(self):
+        """The full-context reading of the probe normaliser: the non-affix rows'
+        attention over their own non-affix keys (held here in the first P_b
+        slots of each request's private pages), merged by LSE with the
+        attention over the affix; the column mass and Top-K then run on the
+        merged LSE.  Returns the extra time of the own-key attention and the
+        merge, and the mean overlap (|A n A'| / K) of the two anchor sets."""
+        w, lay = self.w, self.lay
+        na, na_off = [], [0]
+        for b in range(w.batch):
+            pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+            P_b = int(lay.row_offsets[b + 1] - lay.row_offsets[b])
+            na += [int(pp[i // w.page_size]) * w.page_size + i % w.page_size for i in range(P_b)]
+            na_off.append(len(na))
+        i32 = lambda a: gen.to_device_i32(a, self.dev)
+        na, na_off, row_off = i32(na), i32(na_off), i32(lay.row_offsets)
+        max_p = int(np.diff(lay.row_offsets).max())
+        o_na = torch.empty_like(self.q)
+        lse_na = torch.empty_like(self.lse_aff)
+        A.acache_probe_attention(self.k, self.v, self.q, self.shared_slots, self.lse_aff, o_aff=self.o_aff)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        A.acache_mapped_attention(self.k, self.v, self.q, row_off, na, na_off, o_na, lse=lse_na,
+                                  max_q_per_req=max_p, max_kv_per_req=max_p)
+        A.acache_lse_merge(self.lse_aff, lse_na, self.lse_aff, self.o_aff, o_na, self.o_aff)
+        ev[1].record()
+        scores = torch.zeros_like(self.scores)
+        A.acache_probe_column_mass(self.k, self.v, self.q, self.masked_rows, self.masked_offsets, self.shared_slots,
+                                   self.lse_aff, scores, max_masked=w.m, workspace=self.ws)
+        an_full = torch.empty_like(self.anchors)
+        A.acache_topk_anchors(scores, self.K, w.affix_l, an_full)
+        torch.cuda.synchronize()
+        a1, a2 = self.anchors.cpu().numpy(), an_full.cpu().numpy()
+        overlap = float(np.mean([len(set(a1[b]) & set(a2[b])) / max(self.K, 1) for b in range(w.batch)]))
+        del o_na, lse_na
+        return ev[0].elapsed_time(ev[1]), overlap
+
     def single_pass_ms(self, reps):
         """The same read-slot attention through the single-pass entry point
         (every request streams its whole read list), timed on its own."""
@@ -303,6 +340,7 @@ def main():
     single_ms = S.single_pass_ms(max(3, args.steps // 2))
     rc_ms = S.recompute_ms(3)
     dropna_ms = S.dropna_ms(max(3, args.steps // 2))
+    fn_ms, fn_overlap = S.full_normaliser()
     fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(Setup.STAGES)}
@@ -339,6 +377,7 @@ def main():
         "mapped_attention_single_pass_ms": single_ms,
         "recompute_attention_ms": rc_ms,
         "dropna_mapped_attention_ms": dropna_ms,
+        "full_normaliser": {"extra_ms": fn_ms, "anchor_overlap_with_affix_only": fn_overlap},
         "kv_footprint_gb": {"shared": fp["shared"] / 1e9, "private": fp["private"] / 1e9,
                             "dense": fp["dense"] / 1e9,
                             "acache_saving": 1 - (fp["shared"] + fp["private"]) / fp["dense"]},

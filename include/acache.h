@@ -295,6 +295,24 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                    acache_stream_t stream);
 
 /*
+ * Merge of two attentions of the same query rows over disjoint key sets, as
+ * one softmax over their union.  Used for the full-context reading of the
+ * probe normaliser (Eq. (4), Section 3.2): the non-affix rows' attention
+ * over the affix (acache_probe_attention) merged with their attention over
+ * their own non-affix keys (acache_mapped_attention), whose merged LSE then
+ * feeds acache_probe_column_mass.  For every (row, head) pair i:
+ *   lse[i] = log(exp(lse_a[i]) + exp(lse_b[i]))            (natural log),
+ *   o[i][:] = exp(lse_a[i] - lse[i]) o_a[i][:] + exp(lse_b[i] - lse[i]) o_b[i][:],
+ * and o = 0, lse = -inf when both parts are empty (-inf).
+ *  o_a, o_b, o  [n_pairs][head_dim] of `dtype` (nullable together: LSE only);
+ *  lse_a, lse_b, lse  [n_pairs] fp32.  o may be o_a and lse may be lse_a.
+ * EINVAL for NULL LSE pointers, a partial set of O pointers or n_pairs < 0;
+ * ESHAPE for head_dim outside {16, 32, 64, 128}; EALIGN for O pointers.
+ */
+int acache_lse_merge(int32_t dtype, int64_t n_pairs, int32_t head_dim, const void* o_a, const float* lse_a,
+                     const void* o_b, const float* lse_b, void* o, float* lse, acache_stream_t stream);
+
+/*
  * KV-cache footprint with every request resident (host arithmetic; all
  * pointers host).  Section 4.1: one shared region holds the affix once and
  * each request's private region holds its recompute set R_b (anchors and

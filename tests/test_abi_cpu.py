@@ -218,3 +218,18 @@ def test_kv_footprint_matches_oracle():
             A.acache_kv_footprint(a["seq_len"], a["L"], a["K"], a["page_size"], 2, 3, 8)
     with pytest.raises(A.AcacheError):
         A.acache_kv_footprint([100], 64, 13, 16, 2, 3, 8, 7)
+
+
+def test_lse_merge_validation():
+    lib = Bd._lib()
+    mg = lambda **kw: lib.acache_lse_merge(kw.get("dt", 1), kw.get("n", 4), kw.get("d", 128), kw.get("oa", FAKE),
+                                           kw.get("la", FAKE), kw.get("ob", FAKE), kw.get("lb", FAKE),
+                                           kw.get("o", FAKE), kw.get("l", FAKE), None)
+    assert mg(n=0) == 0
+    assert mg(dt=3) == -2
+    assert mg(d=96) == -3
+    assert mg(n=-1) == -1
+    assert mg(la=None) == -1 and mg(l=None) == -1
+    assert mg(ob=None) == -1
+    assert mg(oa=None, ob=None, o=None, n=0) == 0
+    assert mg(o=FAKE_MIS) == -9

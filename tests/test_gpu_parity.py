@@ -441,3 +441,102 @@ def test_dropna_attention(idx):
         ok, st = bf16_close(out[n].float().cpu().numpy(), ref)
         assert ok, f"DropNA attention layer {n}: {st}"
         np.testing.assert_allclose(lse[n].cpu().numpy(), rl, atol=1e-4)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 32)])
+def test_lse_merge_seeded(dtype, d):
+    """The merge of two attentions over disjoint key sets against the
+    oracle's definition, with empty parts (-inf) and in-place outputs."""
+    g = torch.Generator().manual_seed(11)
+    n, H = 37, 6
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    oa = torch.randn(n, H, d, generator=g).to(dt).to(DEV)
+    ob = torch.randn(n, H, d, generator=g).to(dt).to(DEV)
+    la = (torch.randn(n, H, generator=g) * 3).to(DEV)
+    lb = (torch.randn(n, H, generator=g) * 3).to(DEV)
+    la[0, :] = -math.inf
+    lb[1, :] = -math.inf
+    la[2, :] = -math.inf
+    lb[2, :] = -math.inf
+    h = [np_of(x) for x in (oa, la, ob, lb)]
+    o = torch.empty_like(oa)
+    l = torch.empty_like(la)
+    A.acache_lse_merge(la, lb, l, oa, ob, o)
+    ref_o, ref_l = O.lse_merge(O.decode(h[0]) if dtype == "bf16" else h[0].astype(np.float64), h[1].astype(np.float64),
+                               O.decode(h[2]) if dtype == "bf16" else h[2].astype(np.float64), h[3].astype(np.float64))
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    if dtype == "bf16":
+        ok, st = bf16_close(got, ref_o)
+        assert ok, st
+    else:
+        assert np.abs(got - ref_o).max() <= 1e-5
+    np.testing.assert_allclose(l.cpu().numpy(), ref_l, atol=1e-5)
+    assert (got[2] == 0).all() and np.isneginf(l[2].cpu().numpy()).all()
+    A.acache_lse_merge(la, lb, la, oa, ob, oa)      # in place
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       o.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(la, l)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_probe_full_normaliser_chain(idx):
+    """The full-context reading of the probe normaliser through the library:
+    probe attention over the affix, read-slot attention of the same rows over
+    their own non-affix keys, LSE merge, column mass with the merged LSE.
+    O, LSE and scores against the oracle's one-softmax formulation, and the
+    anchor sets under this reading against the oracle's."""
+    name, w = SMALL[idx]
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 9)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=9)
+    q = gen.make_probe_q(w, lay, device=DEV, seed=9)
+    na, na_off = [], [0]
+    for b in range(w.batch):
+        pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+        P_b = int(lay.row_offsets[b + 1] - lay.row_offsets[b])
+        na += [int(pp[i // w.page_size]) * w.page_size + i % w.page_size for i in range(P_b)]
+        na_off.append(len(na))
+    na, na_off = np.array(na, np.int32), np.array(na_off, np.int32)
+    torch.cuda.synchronize()
+    hk, hv, hq = np_of(k), np_of(v), np_of(q)
+    scale = 1 / math.sqrt(w.head_dim)
+    o_aff = torch.empty_like(q)
+    lse_aff = torch.empty(q.shape[:3], device=DEV)
+    A.acache_probe_attention(k, v, q, i32(lay.shared_slots), lse_aff, o_aff=o_aff)
+    o_na = torch.empty_like(q)
+    lse_na = torch.empty_like(lse_aff)
+    max_p = int(np.diff(lay.row_offsets).max())
+    A.acache_mapped_attention(k, v, q, i32(lay.row_offsets), i32(na), i32(na_off), o_na, lse=lse_na,
+                              max_q_per_req=max_p, max_kv_per_req=max_p)
+    A.acache_lse_merge(lse_aff, lse_na, lse_aff, o_aff, o_na, o_aff)
+    scores = torch.zeros((w.batch, w.L), device=DEV)
+    A.acache_probe_column_mass(k, v, q, i32(lay.masked_rows), i32(lay.masked_offsets), i32(lay.shared_slots),
+                               lse_aff, scores, max_masked=w.m)
+    torch.cuda.synchronize()
+    fp32 = w.dtype == "f32"
+    s_ref = np.zeros((w.batch, w.L))
+    for n in range(w.n_layers):
+        of, lf, sf = O.probe_layer_full(hq[n], hk[n], hv[n], lay.shared_slots, lay.row_offsets, na, na_off,
+                                        w.page_size, w.n_kv_heads, lay.masked_rows, lay.masked_offsets, scale)
+        s_ref += sf
+        got = np_of(o_aff[n]).astype(np.float64) if fp32 else o_aff[n].float().cpu().numpy()
+        if fp32:
+            assert np.abs(got - of).max() <= 1e-5
+        else:
+            # three bf16 roundings stand between this output and the exact one (P inside each part,
+            # each part's O as stored, the merged O), one more than a single attention: 3 * 2^-9 * max|V|
+            ok, st = bf16_close(got, of, max_abs=3 * 2.0 ** -9 * 4.5)
+            assert ok, f"full-normaliser O layer {n}: {st}"
+        np.testing.assert_allclose(lse_aff[n].cpu().numpy(), lf, atol=1e-4)
+    s_gpu = scores.cpu().numpy().astype(np.float64)
+    big = s_ref >= 1e-6 * s_ref.max()
+    assert (np.abs(s_gpu - s_ref)[big] / s_ref[big]).max() <= (1e-5 if fp32 else 1e-3)
+    assert (s_gpu.sum(axis=1) < w.n_layers * w.n_q_heads * np.diff(lay.masked_offsets)).all()
+    an = torch.empty((w.batch, K), dtype=torch.int32, device=DEV)
+    A.acache_topk_anchors(scores, K, w.affix_l, an)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        ok, _ = anchors_match(s_ref[b], an.cpu().numpy()[b], K, w.affix_l)
+        assert ok
