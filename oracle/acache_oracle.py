@@ -314,3 +314,26 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
     wa = np.where(np.isneginf(lse), 0.0, np.exp(lse_a - np.where(np.isneginf(lse), 0.0, lse)))
     wb = np.where(np.isneginf(lse), 0.0, np.exp(lse_b - np.where(np.isneginf(lse), 0.0, lse)))
     return wa[..., None] * o_a + wb[..., None] * o_b, lse
+
+
+# ----------------------------------------------------------------------------
+# CacheBlend-style HKVD selector (Appendix B.5): rank affix tokens by how far
+# their full-prompt KV lies from the affix-only (shared) cache
+# ----------------------------------------------------------------------------
+def hkvd_scores(k_pool, v_pool, shared_slots, k_full, v_full, page_size):
+    """Per request b and affix offset j: the squared L2 norm of the
+    difference between the token's full-prompt K and V (k_full / v_full
+    [N][B][L][Hkv][d]) and its affix-only K and V in the shared region (pool
+    slot shared_slots[j]), summed over layers, KV heads, K and V.  Its Top-K
+    is the Top-K of the norm itself.  Returns [B][L]."""
+    N, B, L, Hkv, d = k_full.shape
+    s = np.zeros((B, L))
+    for n in range(N):
+        for g in range(Hkv):
+            Ka = slot_rows(k_pool[n], shared_slots, g, page_size)      # [L][d]
+            Va = slot_rows(v_pool[n], shared_slots, g, page_size)
+            for b in range(B):
+                dk = decode(k_full[n, b, :, g, :]) - Ka
+                dv = decode(v_full[n, b, :, g, :]) - Va
+                s[b] += (dk * dk).sum(axis=1) + (dv * dv).sum(axis=1)
+    return s

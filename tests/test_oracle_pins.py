@@ -659,3 +659,34 @@ def test_probe_full_normaliser_pins():
         np.testing.assert_allclose(o0, oa, atol=1e-12)
         np.testing.assert_allclose(l0, la, atol=1e-12)
         np.testing.assert_allclose(s0, sa, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# HKVD selector (Appendix B.5)
+# ---------------------------------------------------------------------------
+def test_hkvd_scores_pins():
+    """Zero for a full-prompt cache identical to the shared one; a planted
+    deviation of c on one element of one token adds exactly c^2 there; in
+    general the torch vector norm of the token's whole KV difference,
+    squared."""
+    w = tiny_workload(dtype="f32", segments=(("affix", 20), ("req", 4), ("gen", 4)), batch=3)
+    K, lay, k, v, q = build_case(w)
+    N, Hkv, d, L, B = w.n_layers, w.n_kv_heads, w.head_dim, w.L, w.batch
+    same_k = np.stack([np.stack([np.stack([O.slot_rows(k[n], lay.shared_slots, g, w.page_size) for g in range(Hkv)], 1)
+                                 for _ in range(B)]) for n in range(N)])
+    same_v = np.stack([np.stack([np.stack([O.slot_rows(v[n], lay.shared_slots, g, w.page_size) for g in range(Hkv)], 1)
+                                 for _ in range(B)]) for n in range(N)])
+    assert same_k.shape == (N, B, L, Hkv, d)
+    assert (O.hkvd_scores(k, v, lay.shared_slots, same_k, same_v, w.page_size) == 0).all()
+    pk = same_k.copy()
+    pk[1, 2, 7, 1, 3] += 0.5
+    s = O.hkvd_scores(k, v, lay.shared_slots, pk, same_v, w.page_size)
+    assert s[2, 7] == 0.25 and s.sum() == 0.25
+    rng = np.random.default_rng(5)
+    fk = rng.standard_normal(same_k.shape)
+    fv = rng.standard_normal(same_v.shape)
+    s = O.hkvd_scores(k, v, lay.shared_slots, fk, fv, w.page_size)
+    for b in range(B):
+        for j in range(L):
+            diff = np.concatenate([(fk[:, b, j] - same_k[:, b, j]).ravel(), (fv[:, b, j] - same_v[:, b, j]).ravel()])
+            assert abs(s[b, j] - torch.linalg.vector_norm(torch.from_numpy(diff)).item() ** 2) <= 1e-9 * s[b, j]
