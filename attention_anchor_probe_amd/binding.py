@@ -68,6 +68,7 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                         _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_hkvd_scores": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _I, _P, _P], ctypes.c_int),
     "acache_lse_merge": ([_I, ctypes.c_int64, _I, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "acache_kv_footprint": ([_I, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64),
                              ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
@@ -309,6 +310,17 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention_shared", st)
+
+
+def acache_hkvd_scores(pool_k, pool_v, shared_slots, k_full, v_full, scores, layer_begin=0, stream=None):
+    """HKVD deviation scores.  k_full/v_full: [n_layers][B][L][Hkv][d];
+    scores [B][L] fp32, accumulated."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, B, L = k_full.shape[:3]
+    st = _lib().acache_hkvd_scores(ctypes.byref(pool), _dev(shared_slots, torch.int32), int(L),
+                                   _dev(k_full, pool_k.dtype), _dev(v_full, pool_k.dtype), int(B), int(layer_begin),
+                                   int(n_layers), _dev(scores, torch.float32), _stream(stream))
+    _check("acache_hkvd_scores", st)
 
 
 def acache_lse_merge(lse_a, lse_b, lse, o_a=None, o_b=None, o=None, stream=None):

@@ -459,6 +459,20 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
+int acache_hkvd_scores(const acache_kv_pool* pool, const int32_t* shared_slots, int32_t L, const void* k_full,
+                       const void* v_full, int32_t B, int32_t layer_begin, int32_t n_layers, float* scores,
+                       acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if (B < 0 || L < 0) return ACACHE_EINVAL;
+  if (B == 0 || L == 0 || n_layers == 0) return ACACHE_OK;
+  if (!shared_slots || !k_full || !v_full || !scores) return ACACHE_EINVAL;
+  if (!aligned16(k_full) || !aligned16(v_full)) return ACACHE_EALIGN;
+  return status_of(launch_hkvd(pool->k, pool->v, geom_of(pool), shared_slots, k_full, v_full, B, L, layer_begin,
+                               n_layers, pool->dtype, scores, (hipStream_t)stream));
+}
+
 int acache_lse_merge(int32_t dtype, int64_t n_pairs, int32_t head_dim, const void* o_a, const float* lse_a,
                      const void* o_b, const float* lse_b, void* o, float* lse, acache_stream_t stream) {
   if (dtype != ACACHE_F32 && dtype != ACACHE_BF16) return ACACHE_EDTYPE;

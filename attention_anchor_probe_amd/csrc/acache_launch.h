@@ -103,6 +103,10 @@ hipError_t launch_scatter(void* pool_k, void* pool_v, const void* k_src, const v
 hipError_t launch_lse_merge(int dtype, long long n_pairs, int head_dim, const void* oa, const float* la,
                             const void* ob, const float* lb, void* o, float* l, hipStream_t st);
 
+hipError_t launch_hkvd(const void* pool_k, const void* pool_v, const PoolGeom& geo, const int32_t* shared_slots,
+                       const void* kf, const void* vf, int B, int L, int layer_begin, int n_layers, int dtype,
+                       float* scores, hipStream_t st);
+
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_colmass_generic(const ColmassArgs& a, int dtype, hipStream_t st);
 hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int L, float* scores, hipStream_t st);

@@ -1,4 +1,6 @@
-// Merge of two attentions over disjoint key sets (gfx950): the softmax over
+// Elementwise companions of the ACache attention kernels (gfx950).
+//
+// Merge of two attentions over disjoint key sets: the softmax over
 // the union of the sets weights each part's output by its share of the total
 // exponential mass.  Used for the full-context reading of the probe
 // normaliser of "Affix Cache for Diffusion Large Language Models" (Eq. (4),
@@ -52,6 +54,87 @@ hipError_t launch_lse_merge(int dtype, long long n_pairs, int head_dim, const vo
   else
     hipLaunchKernelGGL(lse_merge_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, (const float*)oa, la,
                        (const float*)ob, lb, (float*)o, l, n_pairs, head_dim);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// CacheBlend-style HKVD selector scores (Appendix B.5 of the same paper): how
+// far each affix token's full-prompt K and V lie from the affix-only cache
+// in the shared region.  One wave per (request, affix offset); every lane
+// sums the squared differences of 8 consecutive elements per step over the
+// token's (KV head, d) block of each layer; one reduction per wave at the
+// end, so the result is deterministic.
+// ---------------------------------------------------------------------------
+namespace {
+template <typename T> struct Ld8;
+template <> struct Ld8<bf16_t> {
+  static __device__ __forceinline__ void run(const bf16_t* p, float* x) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Ld8<float> {
+  static __device__ __forceinline__ void run(const float* p, float* x) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+}  // namespace
+
+template <typename T>
+__global__ __launch_bounds__(256) void hkvd_kernel(const T* __restrict__ pool_k, const T* __restrict__ pool_v,
+                                                   PoolGeom geo, const int32_t* __restrict__ shared_slots,
+                                                   const T* __restrict__ kf, const T* __restrict__ vf, int B, int L,
+                                                   int layer_begin, int n_layers, float* __restrict__ scores) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long tok = (long long)blockIdx.x * 4 + wave;  // b * L + j
+  if (tok >= (long long)B * L) return;
+  const int b = (int)(tok / L), j = (int)(tok - (long long)b * L);
+  const int32_t slot = shared_slots[j];
+  const int d = geo.head_dim, hd = geo.n_kv_heads * d;
+  float acc = 0.f;
+  for (int n = 0; n < n_layers; ++n) {
+    const size_t frow = (((size_t)n * B + b) * L + j) * hd;
+    for (int e = lane * 8; e < hd; e += 512) {
+      const int g = e / d, c = e - g * d;
+      const size_t prow = geo.row(layer_begin + n, slot, g) + c;
+      float a[8], f[8];
+      Ld8<T>::run(pool_k + prow, a);
+      Ld8<T>::run(kf + frow + e, f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += (f[k] - a[k]) * (f[k] - a[k]);
+      Ld8<T>::run(pool_v + prow, a);
+      Ld8<T>::run(vf + frow + e, f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += (f[k] - a[k]) * (f[k] - a[k]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) scores[tok] += acc;
+}
+
+hipError_t launch_hkvd(const void* pool_k, const void* pool_v, const PoolGeom& geo, const int32_t* shared_slots,
+                       const void* kf, const void* vf, int B, int L, int layer_begin, int n_layers, int dtype,
+                       float* scores, hipStream_t st) {
+  const long long tokens = (long long)B * L;
+  if (tokens == 0 || n_layers == 0) return hipSuccess;
+  const long long blocks = (tokens + 3) / 4;
+  if (blocks > (1ll << 31) - 1) return hipErrorInvalidValue;
+  if (dtype == ACACHE_BF16)
+    hipLaunchKernelGGL(hkvd_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t*)pool_k,
+                       (const bf16_t*)pool_v, geo, shared_slots, (const bf16_t*)kf, (const bf16_t*)vf, B, L,
+                       layer_begin, n_layers, scores);
+  else
+    hipLaunchKernelGGL(hkvd_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, (const float*)pool_k,
+                       (const float*)pool_v, geo, shared_slots, (const float*)kf, (const float*)vf, B, L, layer_begin,
+                       n_layers, scores);
   return hipGetLastError();
 }
 

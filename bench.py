@@ -194,6 +194,27 @@ class Setup:
         del o_na, lse_na
         return ev[0].elapsed_time(ev[1]), overlap
 
+    def hkvd_ms(self, reps):
+        """The CacheBlend-style HKVD selector scores (Appendix B.5) of every
+        request's affix tokens over all layers, on synthetic full-prompt K/V
+        of the same shape; timed on its own.  Returns (ms, algorithmic GB)."""
+        w = self.w
+        g = torch.Generator(device=self.dev).manual_seed(5)
+        shape = (w.n_layers, w.batch, w.L, w.n_kv_heads, w.head_dim)
+        kf = torch.randn(shape, generator=g, device=self.dev, dtype=torch.bfloat16)
+        vf = torch.randn(shape, generator=g, device=self.dev, dtype=torch.bfloat16)
+        sc = torch.zeros((w.batch, w.L), device=self.dev)
+        A.acache_hkvd_scores(self.k, self.v, self.shared_slots, kf, vf, sc)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            A.acache_hkvd_scores(self.k, self.v, self.shared_slots, kf, vf, sc)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        gb = (kf.numel() + vf.numel()) * 2 / 1e9 + 2 * w.L * w.n_layers * w.n_kv_heads * w.head_dim * 2 / 1e9
+        del kf, vf, sc
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), gb
+
     def single_pass_ms(self, reps):
         """The same read-slot attention through the single-pass entry point
         (every request streams its whole read list), timed on its own."""
@@ -341,6 +362,7 @@ def main():
     rc_ms = S.recompute_ms(3)
     dropna_ms = S.dropna_ms(max(3, args.steps // 2))
     fn_ms, fn_overlap = S.full_normaliser()
+    hk_ms, hk_gb = S.hkvd_ms(3)
     fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(Setup.STAGES)}
@@ -378,6 +400,7 @@ def main():
         "recompute_attention_ms": rc_ms,
         "dropna_mapped_attention_ms": dropna_ms,
         "full_normaliser": {"extra_ms": fn_ms, "anchor_overlap_with_affix_only": fn_overlap},
+        "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3)},
         "kv_footprint_gb": {"shared": fp["shared"] / 1e9, "private": fp["private"] / 1e9,
                             "dense": fp["dense"] / 1e9,
                             "acache_saving": 1 - (fp["shared"] + fp["private"]) / fp["dense"]},

@@ -295,6 +295,23 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                    acache_stream_t stream);
 
 /*
+ * CacheBlend-style HKVD selector scores (Appendix B.5: the alternative anchor
+ * selector the paper compares against ranks affix tokens by the KV
+ * difference between the affix-only cache and the full-prompt cache):
+ *   scores[b][j] += sum over layers, KV heads and head_dim of
+ *                   (K_full - K_aff)^2 + (V_full - V_aff)^2,
+ * K_aff / V_aff the shared region's rows at slot shared_slots[j] in layer
+ * layer_begin + n, and k_full / v_full [n_layers][B][L][n_kv_heads][head_dim]
+ * (pool dtype, 16-byte aligned) the full-prompt K and V of the affix tokens.
+ * The squared L2 norm of each token's whole KV difference: its Top-K
+ * (acache_topk_anchors) is that of the norm.  scores [B][L] fp32 is
+ * accumulated (zero it first).  Errors as for acache_probe_scores.
+ */
+int acache_hkvd_scores(const acache_kv_pool* pool, const int32_t* shared_slots, int32_t L, const void* k_full,
+                       const void* v_full, int32_t B, int32_t layer_begin, int32_t n_layers, float* scores,
+                       acache_stream_t stream);
+
+/*
  * Merge of two attentions of the same query rows over disjoint key sets, as
  * one softmax over their union.  Used for the full-context reading of the
  * probe normaliser (Eq. (4), Section 3.2): the non-affix rows' attention

@@ -233,3 +233,17 @@ def test_lse_merge_validation():
     assert mg(ob=None) == -1
     assert mg(oa=None, ob=None, o=None, n=0) == 0
     assert mg(o=FAKE_MIS) == -9
+
+
+def test_hkvd_validation():
+    lib = Bd._lib()
+    p = pool()
+    hk = lambda **kw: lib.acache_hkvd_scores(ctypes.byref(kw.pop("pool", p)), kw.get("ss", FAKE), kw.get("L", 32),
+                                             kw.get("kf", FAKE), kw.get("vf", FAKE), kw.get("B", 2),
+                                             kw.get("lb", 0), kw.get("nl", 2), kw.get("s", FAKE), None)
+    assert hk(B=0) == 0 and hk(L=0) == 0 and hk(nl=0) == 0
+    assert hk(B=-1) == -1
+    assert hk(lb=1) == -1
+    assert hk(ss=None) == -1 and hk(s=None) == -1 and hk(kf=None) == -1
+    assert hk(vf=FAKE_MIS) == -9
+    assert hk(pool=pool(dtype=4)) == -2

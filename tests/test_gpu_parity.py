@@ -540,3 +540,35 @@ def test_probe_full_normaliser_chain(idx):
     for b in range(w.batch):
         ok, _ = anchors_match(s_ref[b], an.cpu().numpy()[b], K, w.affix_l)
         assert ok
+
+
+@pytest.mark.parametrize("wl", ["small-f32", "small-bf16", "dream-gqa-L2048"])
+def test_hkvd_scores_and_anchors(wl):
+    """HKVD deviation scores (Appendix B.5) against the oracle, and the anchor
+    sets their Top-K selects."""
+    if wl == "small-f32":
+        w = SMALL[3][1]
+    elif wl == "small-bf16":
+        w = SMALL[1][1]
+    else:
+        w = WORKLOADS[3]
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 4)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=4)
+    dt = gen.TORCH_DT[w.dtype]
+    g = torch.Generator(device=DEV).manual_seed(21)
+    shape = (w.n_layers, w.batch, w.L, w.n_kv_heads, w.head_dim)
+    kf = torch.randn(shape, generator=g, device=DEV).to(dt)
+    vf = torch.randn(shape, generator=g, device=DEV).to(dt)
+    scores = torch.zeros((w.batch, w.L), device=DEV)
+    A.acache_hkvd_scores(k, v, i32(lay.shared_slots), kf, vf, scores)
+    torch.cuda.synchronize()
+    ref = O.hkvd_scores(np_of(k), np_of(v), lay.shared_slots, np_of(kf), np_of(vf), w.page_size)
+    got = scores.cpu().numpy().astype(np.float64)
+    assert (np.abs(got - ref) / ref).max() <= 1e-5
+    an = torch.empty((w.batch, K), dtype=torch.int32, device=DEV)
+    A.acache_topk_anchors(scores, K, w.affix_l, an)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        ok, _ = anchors_match(ref[b], an.cpu().numpy()[b], K, w.affix_l)
+        assert ok
