@@ -93,31 +93,42 @@ __global__ __launch_bounds__(256) void hkvd_kernel(const T* __restrict__ pool_k,
                                                    const T* __restrict__ kf, const T* __restrict__ vf, int B, int L,
                                                    int layer_begin, int n_layers, float* __restrict__ scores) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long tok = (long long)blockIdx.x * 4 + wave;  // b * L + j
+  // j-major: the waves of the B requests of one affix token run together, so
+  // that token's shared rows come from HBM once and then from the caches
+  const long long tok = (long long)blockIdx.x * 4 + wave;  // j * B + b
   if (tok >= (long long)B * L) return;
-  const int b = (int)(tok / L), j = (int)(tok - (long long)b * L);
+  const int j = (int)(tok / B), b = (int)(tok - (long long)j * B);
   const int32_t slot = shared_slots[j];
   const int d = geo.head_dim, hd = geo.n_kv_heads * d;
   float acc = 0.f;
   for (int n = 0; n < n_layers; ++n) {
     const size_t frow = (((size_t)n * B + b) * L + j) * hd;
-    for (int e = lane * 8; e < hd; e += 512) {
-      const int g = e / d, c = e - g * d;
-      const size_t prow = geo.row(layer_begin + n, slot, g) + c;
-      float a[8], f[8];
-      Ld8<T>::run(pool_k + prow, a);
-      Ld8<T>::run(kf + frow + e, f);
+    // four steps' loads are issued before their arithmetic (more loads in flight)
+    for (int e0 = lane * 8; e0 < hd; e0 += 4 * 512) {
+      float a[4][16], f[4][16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc += (f[k] - a[k]) * (f[k] - a[k]);
-      Ld8<T>::run(pool_v + prow, a);
-      Ld8<T>::run(vf + frow + e, f);
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * 512;
+        if (e < hd) {
+          const int g = e / d, c = e - g * d;
+          const size_t prow = geo.row(layer_begin + n, slot, g) + c;
+          Ld8<T>::run(pool_k + prow, a[u]);
+          Ld8<T>::run(kf + frow + e, f[u]);
+          Ld8<T>::run(pool_v + prow, a[u] + 8);
+          Ld8<T>::run(vf + frow + e, f[u] + 8);
+        }
+      }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc += (f[k] - a[k]) * (f[k] - a[k]);
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u * 512 < hd) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) acc += (f[u][k] - a[u][k]) * (f[u][k] - a[u][k]);
+        }
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) scores[tok] += acc;
+  if (lane == 0) scores[(size_t)b * L + j] += acc;
 }
 
 hipError_t launch_hkvd(const void* pool_k, const void* pool_v, const PoolGeom& geo, const int32_t* shared_slots,
