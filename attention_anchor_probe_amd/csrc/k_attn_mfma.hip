@@ -388,6 +388,15 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// A wave-uniform pointer, asserted to the compiler so that it stays in scalar
+// registers (the scalar base of dma16s).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -449,6 +458,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
   const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
   const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
+  const char* kbase_s = uniform_ptr(src.kbase);
+  const char* vbase_s = uniform_ptr(src.vbase);
   // K loads of a tile also record its row offsets (off), which its V loads
   // reuse one iteration later
   auto dma_k = [&](int tile, uint32_t* off) {
@@ -458,13 +469,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       const uint32_t slot = (uint32_t)vs[i];
       // page index and page bytes are below 2^24, their product below 2^32
       off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + src.head_off + ((slot & src.page_mask) << 8);
-      dma16s(src.kbase, off[i] + kchunk[i], st + 4 * i * ROWB);
+      dma16s(kbase_s, off[i] + kchunk[i], st + 4 * i * ROWB);
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(src.vbase, off[i] + vchunk, st + 4 * i * ROWB);
+    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] + vchunk, st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
