@@ -446,36 +446,55 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   const int sel = lane >> 4;
   // slot of the row this lane moves in DMA instruction i of the next K tile
   // (row 16*wave + 4i + lane/16), loaded a tile ahead of its use
+  // Full tiles read their four slots through a buffer resource (lane part
+  // in the vector offset, tile and row-group parts in the scalar offset).  The last, partial tile clamps
+  // its rows to the last key of the list instead, so that every V row it
+  // loads is one of the list's rows (finite; its weight is zero).
   const int32_t* vtable = src.table;
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, nk * 4, 0x00020000);
+  const uint32_t trow = (uint32_t)(16 * wave + sel) * 4;
   int32_t vs[4];
   auto sload = [&](int tile) {
-    const int r0 = tile * RB + 16 * wave + sel;
+    if (tile * RB + RB <= nk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
+      for (int i = 0; i < 4; ++i) vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, tile * (RB * 4) + 16 * i, 0);
+    } else {
+      const int r0 = tile * RB + 16 * wave + sel;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
+    }
   };
-  uint32_t kchunk[4];
+  // global chunk offsets (bits 4..7 of a row offset) of the K and V rows
+  // this lane moves; kvx turns a K offset into the V offset of the same row
+  uint32_t kchunk[4], kvx[4];
+  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;  // row & 3 == sel
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
-  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;                            // row & 3 == sel
+  for (int i = 0; i < 4; ++i) {
+    kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;  // row & 15 == (4i + sel)
+    kvx[i] = kchunk[i] ^ vchunk;
+  }
   const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-  const char* kbase_s = uniform_ptr(src.kbase);
-  const char* vbase_s = uniform_ptr(src.vbase);
-  // K loads of a tile also record its row offsets (off), which its V loads
-  // reuse one iteration later
+  const char* kbase_s = uniform_ptr(src.kbase + src.head_off);
+  const char* vbase_s = uniform_ptr(src.vbase + src.head_off);
+  const uint32_t rmask = src.page_mask << 8;
+  // K loads of a tile also record its row offsets (off, with the K chunk),
+  // which its V loads reuse one iteration later
   auto dma_k = [&](int tile, uint32_t* off) {
     const uint32_t st = lds0 + (tile & 1) * KSTAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t slot = (uint32_t)vs[i];
-      // page index and page bytes are below 2^24, their product below 2^32
-      off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + src.head_off + ((slot & src.page_mask) << 8);
-      dma16s(kbase_s, off[i] + kchunk[i], st + 4 * i * ROWB);
+      // page index and page bytes are below 2^24, their product plus the
+      // row offset below 2^32; the row part (bits 8..) and the chunk part
+      // (bits 4..7) do not overlap
+      off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
+      dma16s(kbase_s, off[i], st + 4 * i * ROWB);
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] + vchunk, st + 4 * i * ROWB);
+    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
