@@ -373,7 +373,11 @@ SharedWs shared_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t n_q, in
                           int32_t n_layers, int32_t max_kv, int32_t L) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   SharedWs w;
-  w.two_pass = mfma_supported(pool->dtype, pool->head_dim) && max_q <= 32;
+  // a decode block whose query-head groups fill a row tile when packed is
+  // MFMA-bound: the single-pass call (which packs them) then serves it
+  // better than the shared-affix kernel, whose gain is HBM reads
+  w.two_pass = mfma_supported(pool->dtype, pool->head_dim) && max_q <= 32 &&
+               gqa_pack(n_q_heads, pool->n_kv_heads, max_q) == 0;
   if (!w.two_pass) return w;
   w.excl_words = 2 * ((L + 63) / 64);
   size_t off = 0;

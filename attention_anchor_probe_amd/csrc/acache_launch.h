@@ -113,6 +113,16 @@ hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int 
 
 // bf16, head_dim 128, MFMA kernels (k_attn_mfma.hip)
 bool mfma_supported(int dtype, int head_dim);
+
+// Query heads per KV head that the many-query MFMA kernel packs into the rows
+// of one unit, or 0 for no packing: packing pays when a KV-head group holds
+// several query heads and either the requests have more than 32 rows or the
+// group's rows fill a 128-row tile (the K/V tiles then serve every head of
+// the group instead of being streamed once per head).
+inline int gqa_pack(int n_q_heads, int n_kv_heads, int max_q) {
+  const int G = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
+  return (G > 1 && (max_q > 32 || (long long)G * max_q >= 128)) ? G : 0;
+}
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st);
 hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st);

@@ -72,6 +72,11 @@ struct AttnP {
   const int32_t* priv_table;
   const int32_t* kv_counts;
   int kv_stride;
+  // attn_rows_mfma only: gpack > 1 packs the query heads of a KV-head group
+  // into the rows of a unit (a unit is then a (layer, KV head, request, row
+  // tile); its rows are the pairs (head g*gpack + j, query i), j-major), so
+  // that every K/V tile serves all heads of the group
+  int gpack;
 };
 
 struct ColP {
@@ -646,33 +651,46 @@ __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
   __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
+  const bool packed = p.gpack > 1;
+  const int n_uh = packed ? p.geo.n_kv_heads : p.n_q_heads;  // heads that index units
   int r = unit;
   const int t = r % p.q_tiles;
   r /= p.q_tiles;
   const int b = r % p.B;
   r /= p.B;
-  const int h = r % p.n_q_heads;
-  const int n = r / p.n_q_heads;
-  const int g = h / (p.n_q_heads / p.geo.n_kv_heads);
+  const int hu = r % n_uh;
+  const int n = r / n_uh;
+  const int g = packed ? hu : hu / (p.n_q_heads / p.geo.n_kv_heads);
   const int layer = p.layer_begin + n;
   int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
   if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
   if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
-  const int rbase = q0 + t * 128;
-  if (rbase >= q1) return;
+  const int nq = q1 - q0;
+  const int rows = packed ? p.gpack * nq : nq;  // rows of this (request, head or group)
+  const int rbase = t * 128;
+  if (rbase >= rows) return;
   const int nk = k1 - k0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, l32 = lane & 31;
-  const int qrow = rbase + wave * 32 + l32;
-  const bool qvalid = qrow < q1;
-  const bool wave_live = rbase + wave * 32 < q1;
+  const int lrow = rbase + wave * 32 + l32;
+  const bool qvalid = lrow < rows;
+  const bool wave_live = rbase + wave * 32 < rows;
+  // this lane's query row and head (rows >= 1 here, so nq >= 1); lanes past
+  // the rows take the first row and head of the unit, whose Q they load but
+  // whose results they never store
+  int qrow = q0 + (qvalid ? lrow : 0), h = hu;
+  if (packed) {
+    const int j = qvalid ? lrow / nq : 0;
+    qrow = q0 + (qvalid ? lrow - j * nq : 0);
+    h = g * p.gpack + j;
+  }
 
   // Q as the B operand of S^T = K Q^T
   bf16x8 qf[8];
   {
-    const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : q0)) * p.n_q_heads + h) * D + g2 * 8;
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D + g2 * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
@@ -1053,16 +1071,22 @@ bool mfma_supported(int dtype, int head_dim) { return dtype == ACACHE_BF16 && he
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   const int B = a.q_offsets ? a.B : 1;
-  const bool split = a.max_q <= 32;
+  const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
+  const bool split = G == 0 && a.max_q <= 32;
   const int RT = split ? 32 : 128;
-  AttnP p;
+  if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
+  const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
+  AttnP p{};
   p.q = (const bf16_t*)a.q;
   p.pool_k = (const bf16_t*)a.pool_k;
   p.pool_v = (const bf16_t*)a.pool_v;
   p.geo = a.geo;
   p.q_offsets = a.q_offsets;
   p.n_q = a.n_q;
-  p.q_tiles = (a.max_q + RT - 1) / RT;
+  const long long q_tiles = (rows + RT - 1) / RT;
+  if (q_tiles > (1ll << 30)) return hipErrorInvalidValue;
+  p.q_tiles = (int)q_tiles;
+  p.gpack = G;
   p.kv_table = a.kv_table;
   p.kv_offsets = a.kv_offsets;
   p.n_kv = a.n_kv;
@@ -1074,7 +1098,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   p.c2 = a.scale * kLog2e;
   p.out = (bf16_t*)a.out;
   p.lse = a.lse;
-  const long long units = (long long)a.n_layers * a.n_q_heads * B * p.q_tiles;
+  const long long units = (long long)a.n_layers * (G > 0 ? a.geo.n_kv_heads : a.n_q_heads) * B * q_tiles;
   if (units == 0) return hipSuccess;
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;

@@ -49,9 +49,16 @@ def parse():
     ap.add_argument("--steps-only", action="store_true",
                     help="skip the measurements after the timed steps (single-pass, recompute, DropNA, "
                          "full-normaliser and HKVD timings), so that a profile holds the steps' launches only")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also time a large library bf16 GEMM and torch's fused attention at the probe's per-layer "
+                         "shape on the same GPU: context for the probe kernel's MFMA rate, not part of the path")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     return ap.parse_args()
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 class Setup:
@@ -218,6 +225,70 @@ class Setup:
         del kf, vf, sc
         return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), gb
 
+    def probe_single_request(self, reps):
+        """The probe of one request alone at the same shapes (its non-affix
+        rows over the affix in all layers, the column mass of its masked rows,
+        its Top-K): the cost a request pays when no other request shares the
+        affix.  Returns the mean ms of each part."""
+        w, lay = self.w, self.lay
+        r0, r1 = int(lay.row_offsets[0]), int(lay.row_offsets[1])
+        m0, m1 = int(lay.masked_offsets[0]), int(lay.masked_offsets[1])
+        i32 = lambda a: gen.to_device_i32(np.asarray(a, np.int32), self.dev)
+        q1 = self.q[:, r0:r1].contiguous()
+        o1 = torch.empty_like(q1)
+        lse1 = torch.empty(q1.shape[:3], device=self.dev)
+        mrows, moff = i32(lay.masked_rows[m0:m1] - r0), i32([0, m1 - m0])
+        sc = torch.zeros((1, w.L), device=self.dev)
+        ws = torch.empty(A.acache_probe_column_mass_workspace_bytes(1, w.L, w.n_q_heads, w.n_layers),
+                         dtype=torch.uint8, device=self.dev)
+        an = torch.empty((1, self.K), dtype=torch.int32, device=self.dev)
+
+        def run(ev):
+            ev[0].record()
+            A.acache_probe_attention(self.k, self.v, q1, self.shared_slots, lse1, o_aff=o1)
+            ev[1].record()
+            sc.zero_()
+            A.acache_probe_column_mass(self.k, self.v, q1, mrows, moff, self.shared_slots, lse1, sc,
+                                       max_masked=m1 - m0, workspace=ws)
+            ev[2].record()
+            A.acache_topk_anchors(sc, self.K, w.affix_l, an)
+            ev[3].record()
+        run([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for ev in evs:
+            run(ev)
+        torch.cuda.synchronize()
+        part = lambda j: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]))
+        res = {"attention_ms": part(0), "column_mass_ms": part(1), "topk_ms": part(2)}
+        res["ms"] = sum(res.values())
+        del q1, o1, lse1, ws
+        return res
+
+    def mapped_cold_warm(self, reps, flush_mib=512):
+        """The shared-affix read-slot attention timed warm (calls back to back)
+        and cold (a flush_mib MiB buffer written between calls, so that no
+        K/V row is left in L2 or the memory-side cache); median ms of each."""
+        w = self.w
+        run = lambda: A.acache_mapped_attention_shared(
+            self.k, self.v, self.qd, self.q_off, self.read_slot, self.kv_offsets, self.shared_slots, self.out,
+            affix_l=w.affix_l, max_q_per_req=w.block_len, max_kv_per_req=w.T, workspace=self.ws_map)
+        flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=self.dev)
+        res = {}
+        for mode in ("warm", "cold"):
+            ts = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                run()
+                b.record()
+                ts.append((a, b))
+            torch.cuda.synchronize()
+            res[f"{mode}_ms"] = float(np.median([a.elapsed_time(b) for a, b in ts]))
+        del flush
+        return res
+
     def single_pass_ms(self, reps):
         """The same read-slot attention through the single-pass entry point
         (every request streams its whole read list), timed on its own."""
@@ -320,6 +391,46 @@ def cpu_baseline(w, S, host, target_s=10.0):
             "seconds": t_map + t_probe}
 
 
+def library_ceilings(w, dev, reps=10):
+    """What the installed libraries reach on this GPU for the same kind of
+    work: a 16384^3 bf16 GEMM (hipBLASLt through torch.matmul) and torch's
+    fused attention kernels (flash and memory-efficient backends only, never
+    the unfused math path) over one layer of the probe: all requests' non-affix
+    rows of one request's shape against the affix, every head."""
+    import torch.nn.functional as F
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+
+    def t(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    res = {}
+    n = 16384
+    x = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    res["gemm_16384_bf16_tflops"] = 2.0 * n ** 3 / t(lambda: x @ y) / 1e9
+    del x, y
+    q = torch.randn(w.batch, w.n_q_heads, w.P, w.head_dim, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(w.batch, w.n_q_heads, w.L, w.head_dim, device=dev, dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    flop = 4.0 * w.batch * w.n_q_heads * w.P * w.L * w.head_dim
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                ms = t(lambda: F.scaled_dot_product_attention(q, k, v))
+            res[f"sdpa_{name}_tflops"] = flop / ms / 1e9
+        except RuntimeError as e:
+            res[f"sdpa_{name}_unavailable"] = str(e)[:120]
+    del q, k, v
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -332,6 +443,7 @@ def main():
     dev = "cuda:0"
     w = WORKLOADS[args.workload]
     S = Setup(w, dev)
+    progress(f"inputs of {w.name} resident")
     host = None
     if not args.no_cpu_baseline:
         def np_of(t):
@@ -351,6 +463,7 @@ def main():
     for _ in range(args.warmup):
         S.step(mk())
     torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up steps done")
     evs = [mk() for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -361,14 +474,22 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    progress(f"{args.steps} timed steps done ({total_ms / args.steps:.2f} ms/step)")
     extras = {}
     if not args.steps_only:
         single_ms = S.single_pass_ms(max(3, args.steps // 2))
         rc_ms = S.recompute_ms(3)
         dropna_ms = S.dropna_ms(max(3, args.steps // 2))
+        progress("single-pass, recompute and DropNA timings done")
         fn_ms, fn_overlap = S.full_normaliser()
         hk_ms, hk_gb = S.hkvd_ms(3)
+        progress("full-context normaliser and HKVD timings done")
+        single_req = S.probe_single_request(max(3, args.steps // 2))
+        cold_warm = S.mapped_cold_warm(max(5, args.steps))
+        progress("single-request probe and cold/warm timings done")
         extras = {
+            "probe_single_request": single_req,
+            "mapped_attention_cold_warm": cold_warm,
             "mapped_attention_single_pass_ms": single_ms,
             "recompute_attention_ms": rc_ms,
             "recompute_attention_tflops": work_model(w, S.K)["recompute_flops"] / (rc_ms * 1e-3) / 1e12,
@@ -377,8 +498,10 @@ def main():
             "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3)},
         }
     fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
-    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                for j, name in enumerate(Setup.STAGES)}
+    stage_t = {name: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+               for j, name in enumerate(Setup.STAGES)}
+    stage_ms = {name: float(np.mean(t)) for name, t in stage_t.items()}
+    stage_pct = {q: {name: float(np.percentile(t, q)) for name, t in stage_t.items()} for q in (10, 50, 90)}
     wm = work_model(w, S.K)
     t_map = stage_ms["mapped_attention"] * 1e-3
     t_probe = stage_ms["probe_attention"] * 1e-3
@@ -416,10 +539,15 @@ def main():
         "probe_attention_tflops": probe_tflops,
         "admission_scatter_gbs": scatter_gbs,
         "stage_ms": stage_ms,
+        "stage_ms_p10": stage_pct[10],
+        "stage_ms_median": stage_pct[50],
+        "stage_ms_p90": stage_pct[90],
         "roofline": roof,
         "roofline_mapped": roof_mapped,
     }
     out.update(extras)
+    if args.ceilings:
+        out["library_ceilings"] = library_ceilings(w, dev)
     if host is not None:
         out["cpu_baseline"] = cpu_baseline(w, S, host)
     print(json.dumps(out), flush=True)

@@ -255,14 +255,17 @@ def test_mapped_attention_ragged(dtype, d):
         np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
 
 
+@pytest.mark.parametrize("hkv", [2, 4], ids=["g4-packed", "g2-shared-kernel"])
 @pytest.mark.parametrize("case", ["mixed", "no-affix", "all-private", "short", "many"])
-def test_shared_affix_attention_seeded(case):
+def test_shared_affix_attention_seeded(case, hkv):
     """The shared-affix entry point on read tables that route a random part of
     the affix to the shared slots and the rest anywhere in the pool, with
     ragged queries (an empty request, a single row, B not a multiple of 4)
     and contexts (one shorter than the affix end, an empty one).  Its result
-    is defined by the read table alone: same oracle as acache_mapped_attention."""
-    w = Workload(101, "sh", "bf16", 2, 8, 2, 128, (("req", 40), ("affix", 333), ("gen", 64)), 7, 0.2,
+    is defined by the read table alone: same oracle as acache_mapped_attention.
+    With 4 query heads per KV head a 32-row block fills a packed 128-row tile
+    and the call runs the single pass; with 2 it runs the shared-affix kernel."""
+    w = Workload(101, "sh", "bf16", 2, 8, hkv, 128, (("req", 40), ("affix", 333), ("gen", 64)), 7, 0.2,
                  page_order="random")
     K = A.acache_anchor_count(w.L, w.rate)
     lay = gen.make_layout(w, K, 5)
@@ -303,6 +306,48 @@ def test_shared_affix_attention_seeded(case):
         live[q_off[4]:q_off[5]] = False    # empty context
         ok, st = bf16_close(o[live], ref[live])
         assert ok, st
+        assert (o[~live] == 0).all()
+        lg = lse[n].cpu().numpy()
+        assert np.isneginf(lg[~live]).all()
+        np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
+
+
+@pytest.mark.parametrize("hq,hkv", [(28, 4), (8, 2), (8, 4)], ids=["g7-packed", "g4-packed", "g2-unpacked"])
+def test_gqa_decode_attention_packed(hq, hkv):
+    """Decode blocks of grouped-query heads: with hq/hkv query heads per KV
+    head and 32-row blocks, groups of 7 and 4 fill a 128-row tile and run
+    packed (a unit's rows are (head, query) pairs of one KV-head group, the
+    last tile partly empty); a group of 2 runs unpacked.  Ragged blocks (an
+    empty one, a single row, rows not a multiple of 32) and contexts (one
+    key, an empty context, one over several tiles with a ragged tail)."""
+    w = Workload(103, "gq", "bf16", 2, hq, hkv, 128, (("req", 30), ("affix", 200), ("gen", 64)), 6, 0.2,
+                 page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 7)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=7)
+    nslot = lay.n_pages * w.page_size
+    rng = np.random.default_rng(23)
+    q_counts = [32, 0, 17, 1, 32, 9]
+    kv_counts = [294, 40, 1, 0, 130, 777]
+    read = np.concatenate([rng.integers(0, nslot, c) for c in kv_counts]).astype(np.int32)
+    q_off = np.concatenate([[0], np.cumsum(q_counts)]).astype(np.int32)
+    kv_off = np.concatenate([[0], np.cumsum(kv_counts)]).astype(np.int32)
+    qd = gen.make_rows(w, int(q_off[-1]), gen.S_QDEC, device=DEV, heads=w.n_q_heads, seed=7)
+    torch.cuda.synchronize()
+    kh, vh, qh = np_of(k), np_of(v), np_of(qd)
+    out = torch.full_like(qd, 7.0)
+    lse = torch.empty(qd.shape[:3], device=DEV)
+    A.acache_mapped_attention(k, v, qd, i32(q_off), i32(read), i32(kv_off), out, lse=lse,
+                              max_q_per_req=max(q_counts), max_kv_per_req=max(kv_counts))
+    torch.cuda.synchronize()
+    live = np.ones(int(q_off[-1]), bool)
+    live[q_off[3]:q_off[4]] = False        # empty context
+    for n in range(w.n_layers):
+        ref, rl = O.mapped_attention_layer(qh[n], kh[n], vh[n], q_off, read, kv_off, w.n_kv_heads, w.page_size,
+                                           1 / math.sqrt(w.head_dim))
+        o = out[n].float().cpu().numpy()
+        ok, st = bf16_close(o[live], ref[live])
+        assert ok, (n, st)
         assert (o[~live] == 0).all()
         lg = lse[n].cpu().numpy()
         assert np.isneginf(lg[~live]).all()
