@@ -393,7 +393,8 @@ def cpu_baseline(w, S, host, target_s=10.0):
 
 def library_ceilings(w, dev, reps=10):
     """What the installed libraries reach on this GPU for the same kind of
-    work: a 16384^3 bf16 GEMM (hipBLASLt through torch.matmul) and torch's
+    work: a plain 4 GiB device copy (GB/s of bytes read plus written), a
+    16384^3 bf16 GEMM (hipBLASLt through torch.matmul) and torch's
     fused attention kernels (flash and memory-efficient backends only, never
     the unfused math path) over one layer of the probe: all requests' non-affix
     rows of one request's shape against the affix, every head."""
@@ -411,6 +412,11 @@ def library_ceilings(w, dev, reps=10):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
     res = {}
+    # a plain 4 GiB device copy (read + write bytes): the practical HBM rate
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    res["device_copy_gbs"] = 2.0 * src.numel() / t(lambda: dst.copy_(src)) / 1e6
+    del src, dst
     n = 16384
     x = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     y = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
