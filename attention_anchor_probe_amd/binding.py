@@ -68,6 +68,10 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                         _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_store_attend_workspace_bytes": ([ctypes.POINTER(KVPool), _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+                                            ctypes.c_int),
+    "acache_store_attend": ([ctypes.POINTER(KVPool), _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                             _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "acache_hkvd_scores": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _I, _P, _P], ctypes.c_int),
     "acache_lse_merge": ([_I, ctypes.c_int64, _I, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "acache_kv_footprint": ([_I, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64),
@@ -310,6 +314,44 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention_shared", st)
+
+
+def acache_store_attend_workspace_bytes(pool_k, pool_v, *, B, max_q_per_req, max_kv_per_req):
+    pool = make_pool(pool_k, pool_v)
+    ws_bytes = ctypes.c_size_t()
+    _check("acache_store_attend_workspace_bytes",
+           _lib().acache_store_attend_workspace_bytes(ctypes.byref(pool), int(B), int(max_q_per_req),
+                                                      int(max_kv_per_req), ctypes.byref(ws_bytes)))
+    return ws_bytes.value
+
+
+def acache_store_attend(pool_k, pool_v, k_src, v_src, src_pos, src_slot, src_offsets, q, q_offsets, read_slot,
+                        kv_offsets, out, *, max_q_per_req, max_kv_per_req, lse=None, layer_begin=0, scale=None,
+                        workspace=None, stream=None):
+    """Store the source rows to their private slots and attend through the
+    read-slot map (same result as acache_scatter_private followed by
+    acache_mapped_attention).  k_src/v_src: [n_layers][n_src][Hkv][d];
+    src_pos/src_slot [n_src]; src_offsets [B+1]; q/out: [n_layers][n_q][Hq][d]."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_q, hq, d = q.shape
+    B = q_offsets.numel() - 1
+    n_src = src_slot.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        nb = acache_store_attend_workspace_bytes(pool_k, pool_v, B=B, max_q_per_req=max_q_per_req,
+                                                 max_kv_per_req=max_kv_per_req)
+        if nb > 0:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    st = _lib().acache_store_attend(
+        ctypes.byref(pool), _dev(k_src, pool_k.dtype), _dev(v_src, pool_k.dtype), _dev(src_pos, torch.int32),
+        _dev(src_slot, torch.int32), _dev(src_offsets, torch.int32), n_src, _dev(q, pool_k.dtype),
+        _dev(q_offsets, torch.int32), n_q, int(max_q_per_req), _dev(read_slot, torch.int32),
+        _dev(kv_offsets, torch.int32), int(max_kv_per_req), B, hq, layer_begin, n_layers, float(scale),
+        _dev(out, pool_k.dtype), _dev(lse, torch.float32),
+        _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
+        _stream(stream))
+    _check("acache_store_attend", st)
 
 
 def acache_hkvd_scores(pool_k, pool_v, shared_slots, k_full, v_full, scores, layer_begin=0, stream=None):

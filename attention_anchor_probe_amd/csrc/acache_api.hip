@@ -463,6 +463,97 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
+namespace {
+// workspace of the fused store-then-attend path (256-byte aligned parts)
+struct StoreWs {
+  bool fused = false;
+  int stride = 0;
+  size_t other = 0, counts = 0, total = 0;
+};
+
+StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, int32_t max_kv) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  StoreWs w;
+  w.fused = mfma_supported(pool->dtype, pool->head_dim) && max_q > 0 && max_kv <= kStorePlanMaxKv;
+  if (!w.fused) return w;
+  w.stride = max_kv;
+  w.other = 0;
+  w.counts = up((size_t)B * w.stride * 4);
+  w.total = w.counts + up((size_t)B * 4);
+  return w;
+}
+}  // namespace
+
+int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t max_q_per_req,
+                                        int32_t max_kv_per_req, size_t* bytes) {
+  int st;
+  if (!bytes) return ACACHE_EINVAL;
+  if ((st = check_pool(pool))) return st;
+  if (B < 0 || max_q_per_req < 0 || max_kv_per_req < 0) return ACACHE_EINVAL;
+  *bytes = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req).total;
+  return ACACHE_OK;
+}
+
+int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const void* v_src, const int32_t* src_pos,
+                        const int32_t* src_slot, const int32_t* src_offsets, int32_t n_src, const void* q,
+                        const int32_t* q_offsets, int32_t n_q, int32_t max_q_per_req, const int32_t* read_slot,
+                        const int32_t* kv_offsets, int32_t max_kv_per_req, int32_t B, int32_t n_q_heads,
+                        int32_t layer_begin, int32_t n_layers, float scale, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if ((st = check_heads(pool, n_q_heads))) return st;
+  if (B < 0 || n_src < 0 || n_q < 0 || max_q_per_req < 0 || max_q_per_req > n_q || max_kv_per_req < 0)
+    return ACACHE_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
+  if (B > 65535) return ACACHE_ESHAPE;
+  if (n_src > 0 && (!k_src || !v_src || !src_pos || !src_slot || !src_offsets)) return ACACHE_EINVAL;
+  if (n_src > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
+  const StoreWs w = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req);
+  if (!w.fused || B == 0 || n_q == 0 || n_layers == 0) {
+    // the definition itself: the scatter, then the attention through read_slot
+    if ((st = acache_scatter_private(pool, k_src, v_src, src_slot, n_src, layer_begin, n_layers, stream)))
+      return st;
+    return acache_mapped_attention(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                   n_q_heads, layer_begin, n_layers, scale, out, lse, nullptr, 0, stream);
+  }
+  if (!q || !q_offsets || !kv_offsets || !out || !src_offsets) return ACACHE_EINVAL;
+  if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return ACACHE_EALIGN;
+  if (!workspace || workspace_bytes < w.total) return ACACHE_EWORKSPACE;
+  if (!aligned16(workspace)) return ACACHE_EALIGN;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_store_plan(read_slot, kv_offsets, src_pos, src_offsets, B, max_kv_per_req, w.stride,
+                                   (int32_t*)(ws + w.other), (int32_t*)(ws + w.counts), s);
+  if (e != hipSuccess) return status_of(e);
+  StoreAttnArgs a;
+  a.q = q;
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.geo = geom_of(pool);
+  a.q_offsets = q_offsets;
+  a.n_q = n_q;
+  a.max_q = max_q_per_req;
+  a.other_slots = (const int32_t*)(ws + w.other);
+  a.other_counts = (const int32_t*)(ws + w.counts);
+  a.other_stride = w.stride;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.src_slot = src_slot;
+  a.src_offsets = src_offsets;
+  a.n_src = n_src;
+  a.B = B;
+  a.n_q_heads = n_q_heads;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  return status_of(launch_attn_mfma_store(a, s));
+}
+
 int acache_hkvd_scores(const acache_kv_pool* pool, const int32_t* shared_slots, int32_t L, const void* k_full,
                        const void* v_full, int32_t B, int32_t layer_begin, int32_t n_layers, float* scores,
                        acache_stream_t stream) {

@@ -150,6 +150,32 @@ class Setup:
         del qr, orc
         return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
+    def store_attend_ms(self, reps):
+        """The admission's store-then-attend in one call (Section 4.3): the
+        recomputed K/V rows of every request are stored to their private slots
+        and the recompute-phase queries attend through the read-slot map,
+        reading those rows from the source; timed on its own."""
+        w = self.w
+        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads)
+        orc = torch.empty_like(qr)
+        max_r = int(np.diff(self.lay.rc_offsets).max())
+        rc_off = self._keep[5]
+        nb = A.acache_store_attend_workspace_bytes(self.k, self.v, B=w.batch, max_q_per_req=max_r,
+                                                   max_kv_per_req=w.T)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.dev)
+        run = lambda: A.acache_store_attend(self.k, self.v, self.src_k, self.src_v, self.rc_pos, self.rc_slot, rc_off,
+                                            qr, rc_off, self.read_slot, self.kv_offsets, orc, max_q_per_req=max_r,
+                                            max_kv_per_req=w.T, workspace=ws)
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        del qr, orc, ws
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
     def dropna_ms(self, reps):
         """Decode-block attention under the DropNA ablation (Section 5.3): the
         same queries over the recompute map only (the non-anchor affix cache
@@ -482,11 +508,14 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     progress(f"{args.steps} timed steps done ({total_ms / args.steps:.2f} ms/step)")
     extras = {}
+    stage_mean = lambda name: float(np.mean([evs[i][Setup.STAGES.index(name)].elapsed_time(
+        evs[i][Setup.STAGES.index(name) + 1]) for i in range(args.steps)]))
     if not args.steps_only:
         single_ms = S.single_pass_ms(max(3, args.steps // 2))
         rc_ms = S.recompute_ms(3)
+        sa_ms = S.store_attend_ms(3)
         dropna_ms = S.dropna_ms(max(3, args.steps // 2))
-        progress("single-pass, recompute and DropNA timings done")
+        progress("single-pass, recompute, store-then-attend and DropNA timings done")
         fn_ms, fn_overlap = S.full_normaliser()
         hk_ms, hk_gb = S.hkvd_ms(3)
         progress("full-context normaliser and HKVD timings done")
@@ -499,6 +528,9 @@ def main():
             "mapped_attention_single_pass_ms": single_ms,
             "recompute_attention_ms": rc_ms,
             "recompute_attention_tflops": work_model(w, S.K)["recompute_flops"] / (rc_ms * 1e-3) / 1e12,
+            "store_then_attend": {"one_call_ms": sa_ms,
+                                  "scatter_then_attention_ms": stage_mean("admission_scatter") + rc_ms,
+                                  "tflops": work_model(w, S.K)["recompute_flops"] / (sa_ms * 1e-3) / 1e12},
             "dropna_mapped_attention_ms": dropna_ms,
             "full_normaliser": {"extra_ms": fn_ms, "anchor_overlap_with_affix_only": fn_overlap},
             "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3)},

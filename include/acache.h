@@ -298,6 +298,49 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                    acache_stream_t stream);
 
 /*
+ * Store-then-attend of the recompute phase, Section 4.3 and Appendix C.1:
+ * the recomputed K/V rows are written to their private slots through the
+ * write-side map and the attention reads the full context through the
+ * read-slot map.  The result is defined as
+ *   acache_scatter_private(pool, k_src, v_src, src_slot, n_src, ...);
+ *   acache_mapped_attention(pool, q, q_offsets, ..., read_slot, kv_offsets, ...);
+ * on the same stream: pool slots src_slot[i] hold the source rows afterwards,
+ * and out / lse are those of the attention.
+ *  k_src, v_src [n_layers][n_src][n_kv_heads][head_dim] (pool dtype, 16-byte
+ *               aligned); request b's rows are src_offsets[b] .. src_offsets[b+1]
+ *               (src_offsets [B+1], always given) and row i holds logical
+ *               position src_pos[i] of its request, to be stored at src_slot[i].
+ *  q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req,
+ *  out, lse    as for acache_mapped_attention.
+ * For bf16 pools with head_dim 128 one plan kernel and one attention kernel
+ * run: each request's rows attend to its read list without its src_pos
+ * positions (read from the pool) and to its source rows (read from k_src /
+ * v_src), while one unit per (layer, KV head, request) copies the source rows
+ * to src_slot.  That equals the definition when, as the maps of
+ * acache_build_maps arrange for the recompute set, each src_slot[i] is read at
+ * position src_pos[i] of request b (read_slot[kv_offsets[b] + src_pos[i]] ==
+ * src_slot[i]) and at no other position of any request; keys are then summed
+ * in another order (fp32 rounding only).  Other pools, or calls without
+ * query rows, run the two calls of the definition and need no workspace.
+ * Workspace: size from acache_store_attend_workspace_bytes (given the same
+ * pool, B, max_q_per_req and max_kv_per_req; about 4 * B * max_kv_per_req
+ * bytes), 16-byte aligned, rewritten by every call (calls sharing it must not
+ * overlap).  max_kv_per_req <= 262144 on the fused path.
+ * Errors as for the two calls; EWORKSPACE when the workspace is missing or
+ * small.  Nothing is enqueued when an error is returned.
+ */
+int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t max_q_per_req,
+                                        int32_t max_kv_per_req, size_t* bytes /*host*/);
+
+int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const void* v_src,
+                        const int32_t* src_pos, const int32_t* src_slot, const int32_t* src_offsets,
+                        int32_t n_src, const void* q, const int32_t* q_offsets, int32_t n_q,
+                        int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
+                        int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin,
+                        int32_t n_layers, float scale, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, acache_stream_t stream);
+
+/*
  * CacheBlend-style HKVD selector scores (Appendix B.5: the alternative anchor
  * selector the paper compares against ranks affix tokens by the KV
  * difference between the affix-only cache and the full-prompt cache):

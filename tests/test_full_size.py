@@ -23,6 +23,9 @@ Part B -- maps, scatter, decode blocks and read-slot attention
   * read-slot map, recompute map and block slots: bit-exact for all requests;
   * the pool after the admission scatter and each block store: bit-exact on
     sampled layers (whole layer, including every untouched byte);
+  * the recompute phase on sampled layers: the recomputed rows' attention
+    over their full read lists, then the one-call store-then-attend of a
+    fresh set of rows (the whole pool layer bit-exact, sampled rows' O and LSE);
   * read-slot attention of sampled (layer, request) pairs at every step.
 """
 import math
@@ -197,7 +200,30 @@ def test_full_size(cid):
             ok, st = bf16_close(orc[0][sel].float().cpu().numpy(), o_ref)
             assert ok, f"recompute-phase attention layer {n} request {b}: {st}"
             np.testing.assert_allclose(lrc[0][sel].cpu().numpy(), l_ref, rtol=2e-5, atol=1e-4)
-        del qr, orc, lrc
+        # the same queries through the one-call store-then-attend, storing a
+        # fresh set of recomputed rows: the pool layer equals the oracle's
+        # scatter of them and the attention reads them
+        say(f"store-then-attend, layer {n}")
+        s2k = gen.make_rows(w, n_rc, gen.S_SRC_K, device=DEV, layers=[n], step=1)
+        s2v = gen.make_rows(w, n_rc, gen.S_SRC_V, device=DEV, layers=[n], step=1)
+        torch.cuda.synchronize()
+        h2k, h2v = np_of(s2k), np_of(s2v)
+        A.acache_store_attend(k, v, s2k, s2v, rcp, rcs, keep[5], qr, keep[5], read, keep[4], orc, lse=lrc,
+                              layer_begin=n, max_q_per_req=max_r, max_kv_per_req=w.T)
+        torch.cuda.synchronize()
+        O.scatter(hk[n][None], hv[n][None], h2k, h2v, r_rcslot, w.page_size)
+        assert np.array_equal(np_of(k[n]), hk[n]) and np.array_equal(np_of(v[n]), hv[n]), f"stored pool layer {n}"
+        for b in reqs:
+            r0, r1 = int(lay.rc_offsets[b]), int(lay.rc_offsets[b + 1])
+            rows = r0 + np.array(_sampled(r1 - r0, 48, 500 + b + n))
+            o_ref, l_ref = O.mapped_attention_layer(hqr[rows], hk[n], hv[n], [0, len(rows)],
+                                                    r_read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]], [0, w.T],
+                                                    w.n_kv_heads, w.page_size, scale)
+            sel = torch.as_tensor(rows, device=DEV)
+            ok, st = bf16_close(orc[0][sel].float().cpu().numpy(), o_ref)
+            assert ok, f"store-then-attend layer {n} request {b}: {st}"
+            np.testing.assert_allclose(lrc[0][sel].cpu().numpy(), l_ref, rtol=2e-5, atol=1e-4)
+        del qr, orc, lrc, s2k, s2v
     q_off = np.arange(w.batch + 1) * w.block_len
     for step in range(w.steps):
         say(f"decode step {step}: block slots, block store, read-slot attention (all layers)")

@@ -354,6 +354,61 @@ def test_gqa_decode_attention_packed(hq, hkv):
         np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 4, 4), ("bf16", 128, 8, 2), ("f32", 32, 4, 2)],
+                         ids=["bf16-mha", "bf16-gqa-packed", "f32-two-calls"])
+def test_store_attend_seeded(dtype, d, hq, hkv):
+    """Store-then-attend of the recompute phase (Section 4.3): the pool after
+    the call equals the oracle's scatter byte for byte, and the attention
+    equals the oracle's read-slot attention over that pool.  Maps come from
+    the oracle on seeded anchors.  Request 1 stores nothing (its recompute
+    positions keep the pool's old rows), request 2 has no query rows (its rows
+    must still be stored), request 0 has many query rows over several tiles."""
+    w = Workload(104, "sa", dtype, 2, hq, hkv, d, (("req", 24), ("affix", 300), ("req", 9), ("gen", 64)), 4, 0.2,
+                 page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 9)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=9)
+    scores = gen.seeded_scores(w, seed=9).numpy().astype(np.float64)
+    read, rc_pos, rc_slot, kept = [], [], [], [0]
+    for b in range(w.batch):
+        an = O.topk_anchors(scores[b], K, w.affix_l)
+        pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+        r_, p_, s_ = O.build_maps(an, int(lay.seq_len[b]), w.affix_l, w.L, lay.shared_slots, pp, w.page_size)
+        read.append(r_)
+        if b != 1:
+            rc_pos.append(p_)
+            rc_slot.append(s_)
+        kept.append(kept[-1] + (0 if b == 1 else len(p_)))
+    read, rc_pos, rc_slot = (np.concatenate(x).astype(np.int32) for x in (read, rc_pos, rc_slot))
+    src_off = np.array(kept, np.int32)
+    n_src = int(src_off[-1])
+    src_k = gen.make_rows(w, n_src, gen.S_SRC_K, device=DEV, seed=9)
+    src_v = gen.make_rows(w, n_src, gen.S_SRC_V, device=DEV, seed=9)
+    q_counts = [int(np.diff(lay.rc_offsets)[0]), 33, 0, 17]
+    q_off = np.concatenate([[0], np.cumsum(q_counts)]).astype(np.int32)
+    q = gen.make_rows(w, int(q_off[-1]), gen.S_QRC, device=DEV, heads=w.n_q_heads, seed=9)
+    torch.cuda.synchronize()
+    kh, vh, qh, skh, svh = np_of(k), np_of(v), np_of(q), np_of(src_k), np_of(src_v)
+    out = torch.full_like(q, 7.0)
+    lse = torch.empty(q.shape[:3], device=DEV)
+    A.acache_store_attend(k, v, src_k, src_v, i32(rc_pos), i32(rc_slot), i32(src_off), q, i32(q_off), i32(read),
+                          i32(lay.kv_offsets), out, lse=lse, max_q_per_req=max(q_counts), max_kv_per_req=w.T)
+    torch.cuda.synchronize()
+    kp, vp = kh.copy(), vh.copy()
+    O.scatter(kp, vp, skh, svh, rc_slot, w.page_size)
+    assert np.array_equal(np_of(k), kp) and np.array_equal(np_of(v), vp)
+    for n in range(w.n_layers):
+        ref, rl = O.mapped_attention_layer(qh[n], kp[n], vp[n], q_off, read, lay.kv_offsets, w.n_kv_heads,
+                                           w.page_size, 1 / math.sqrt(d))
+        o = out[n].float().cpu().numpy()
+        if dtype == "f32":
+            assert np.abs(o - ref).max() <= 1e-5
+        else:
+            ok, st = bf16_close(o, ref)
+            assert ok, (n, st)
+        np.testing.assert_allclose(lse[n].cpu().numpy(), rl, atol=1e-4)
+
+
 def test_shared_affix_attention_matches_single_pass_and_repeats():
     """Two calls in a row (the second with fewer requests) agree with the
     single-pass entry point on a maps-built decode step."""
