@@ -58,6 +58,9 @@ PoolGeom geom_of(const acache_kv_pool* p) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? ACACHE_OK : ACACHE_EDEVICE; }
 
+// a dry run that rejects the sizes: a limit of the kernels' 32-bit indexing
+int limits_of(hipError_t e) { return e == hipSuccess ? ACACHE_OK : ACACHE_ESHAPE; }
+
 int check_map_args(const acache_map_args* m) {
   if (!m) return ACACHE_EINVAL;
   if (m->B < 0 || m->L <= 0 || m->affix_l < 0 || m->K < 0 || m->K > m->L || m->max_seq_len < 0)
@@ -140,7 +143,8 @@ int check_probe_common(const acache_kv_pool* pool, const void* q, int32_t n_rows
 
 hipError_t probe_attention_launch(const acache_kv_pool* pool, const void* q, int32_t n_rows,
                                   const int32_t* shared_slots, int32_t L, int32_t n_q_heads, int32_t layer_begin,
-                                  int32_t n_layers, float scale, void* o_aff, float* lse, hipStream_t s) {
+                                  int32_t n_layers, float scale, void* o_aff, float* lse, hipStream_t s,
+                                  bool dry = false) {
   if (n_rows == 0 || n_layers == 0) return hipSuccess;
   AttnArgs a;
   a.q = q;
@@ -161,14 +165,15 @@ hipError_t probe_attention_launch(const acache_kv_pool* pool, const void* q, int
   a.scale = scale;
   a.out = o_aff;
   a.lse = lse;
-  return mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s) : launch_attn_generic(a, pool->dtype, s);
+  if (mfma_supported(pool->dtype, pool->head_dim)) return launch_attn_mfma(a, s, dry);
+  return dry ? hipSuccess : launch_attn_generic(a, pool->dtype, s);
 }
 
 hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, int32_t n_rows,
                                     const int32_t* masked_rows, const int32_t* masked_offsets, int32_t max_masked,
                                     const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
                                     int32_t layer_begin, int32_t n_layers, float scale, const float* lse,
-                                    float* scores, float* partial, hipStream_t s) {
+                                    float* scores, float* partial, hipStream_t s, bool dry = false) {
   if (n_layers == 0 || B == 0) return hipSuccess;
   ColmassArgs c;
   c.q = q;
@@ -188,6 +193,7 @@ hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, i
   c.lse = lse;
   c.partial = partial;
   const bool mf = mfma_supported(pool->dtype, pool->head_dim);
+  if (dry) return mf ? launch_colmass_mfma(c, s, true) : hipSuccess;
   hipError_t e = mf ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
   if (e != hipSuccess) return e;
   return launch_colmass_reduce(partial, mf ? n_layers * n_q_heads : n_layers, B, L, scores, s);
@@ -203,8 +209,12 @@ int acache_probe_attention(const acache_kv_pool* pool, const void* q, int32_t n_
     return st;
   if (!lse_aff) return ACACHE_EINVAL;
   if (o_aff && !aligned16(o_aff)) return ACACHE_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = limits_of(probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers,
+                                             scale, o_aff, lse_aff, s, true))))
+    return st;
   return status_of(probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale,
-                                          o_aff, lse_aff, (hipStream_t)stream));
+                                          o_aff, lse_aff, s));
 }
 
 int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
@@ -224,9 +234,14 @@ int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t 
   acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, &need);
   if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
     return ACACHE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots,
+                                               L, B, n_q_heads, layer_begin, n_layers, scale, lse_aff, scores,
+                                               (float*)workspace, s, true))))
+    return st;
   return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots, L,
                                             B, n_q_heads, layer_begin, n_layers, scale, lse_aff, scores,
-                                            (float*)workspace, (hipStream_t)stream));
+                                            (float*)workspace, s));
 }
 
 int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* masked_rows,
@@ -255,6 +270,13 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
     lse = (float*)ws;
     ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
   }
+  if ((st = limits_of(probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers,
+                                             scale, o_aff, lse, s, true))))
+    return st;
+  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots,
+                                               L, B, n_q_heads, layer_begin, n_layers, scale, lse, scores, (float*)ws,
+                                               s, true))))
+    return st;
   hipError_t e = probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale,
                                         o_aff, lse, s);
   if (e != hipSuccess) return ACACHE_EDEVICE;
@@ -318,11 +340,12 @@ int acache_mapped_attention_workspace_bytes(int32_t B, int32_t n_q, int32_t n_q_
   return ACACHE_OK;
 }
 
-int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
-                            int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
-                            int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin,
-                            int32_t n_layers, float scale, void* out, float* lse, void* workspace,
-                            size_t workspace_bytes, acache_stream_t stream) {
+namespace {
+// acache_mapped_attention: every check, then (dry == false) the launch
+int mapped_attention_impl(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
+                          int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
+                          int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin, int32_t n_layers,
+                          float scale, void* out, float* lse, hipStream_t s, bool dry) {
   int st;
   if ((st = check_pool(pool))) return st;
   if ((st = check_layers(pool, layer_begin, n_layers))) return st;
@@ -330,8 +353,6 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
   if (B < 0 || n_q < 0 || max_q_per_req < 0 || max_q_per_req > n_q || max_kv_per_req < 0) return ACACHE_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
   if (B > 65535) return ACACHE_ESHAPE;
-  (void)workspace;
-  (void)workspace_bytes;
   if (B == 0 || n_q == 0 || n_layers == 0) return ACACHE_OK;
   if (!q || !q_offsets || !kv_offsets || !out) return ACACHE_EINVAL;
   if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
@@ -355,10 +376,21 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
   a.scale = scale;
   a.out = out;
   a.lse = lse;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = mfma_supported(pool->dtype, pool->head_dim) ? launch_attn_mfma(a, s)
-                                                              : launch_attn_generic(a, pool->dtype, s);
-  return status_of(e);
+  if (!mfma_supported(pool->dtype, pool->head_dim)) return dry ? ACACHE_OK : status_of(launch_attn_generic(a, pool->dtype, s));
+  if ((st = limits_of(launch_attn_mfma(a, s, true)))) return st;
+  return dry ? ACACHE_OK : status_of(launch_attn_mfma(a, s));
+}
+}  // namespace
+
+int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
+                            int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
+                            int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin,
+                            int32_t n_layers, float scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, acache_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                               n_q_heads, layer_begin, n_layers, scale, out, lse, (hipStream_t)stream, false);
 }
 
 namespace {
@@ -434,10 +466,6 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   if (!aligned16(workspace)) return ACACHE_EALIGN;
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_shared_plan(read_slot, kv_offsets, shared_slots, B, affix_l, L, max_kv_per_req, w.stride,
-                                    kSharedPrivTile, (int32_t*)(ws + w.priv), (int32_t*)(ws + w.counts),
-                                    (uint32_t*)(ws + w.excl), w.excl_words, s);
-  if (e != hipSuccess) return status_of(e);
   SharedAttnArgs a;
   a.q = q;
   a.pool_k = pool->k;
@@ -460,6 +488,11 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   a.scale = scale;
   a.out = out;
   a.lse = lse;
+  if ((st = limits_of(launch_attn_mfma_shared(a, s, true)))) return st;
+  hipError_t e = launch_shared_plan(read_slot, kv_offsets, shared_slots, B, affix_l, L, max_kv_per_req, w.stride,
+                                    kSharedPrivTile, (int32_t*)(ws + w.priv), (int32_t*)(ws + w.counts),
+                                    (uint32_t*)(ws + w.excl), w.excl_words, s);
+  if (e != hipSuccess) return status_of(e);
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
@@ -512,11 +545,15 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
   if (n_src > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
   const StoreWs w = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req);
   if (!w.fused || B == 0 || n_q == 0 || n_layers == 0) {
-    // the definition itself: the scatter, then the attention through read_slot
-    if ((st = acache_scatter_private(pool, k_src, v_src, src_slot, n_src, layer_begin, n_layers, stream)))
+    // the definition itself: the scatter, then the attention through
+    // read_slot (the attention's arguments are checked before the scatter)
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                    n_q_heads, layer_begin, n_layers, scale, out, lse, s, true)))
       return st;
-    return acache_mapped_attention(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
-                                   n_q_heads, layer_begin, n_layers, scale, out, lse, nullptr, 0, stream);
+    if ((st = acache_scatter_private(pool, k_src, v_src, src_slot, n_src, layer_begin, n_layers, stream))) return st;
+    return mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                 n_q_heads, layer_begin, n_layers, scale, out, lse, s, false);
   }
   if (!q || !q_offsets || !kv_offsets || !out || !src_offsets) return ACACHE_EINVAL;
   if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
@@ -525,9 +562,6 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
   if (!aligned16(workspace)) return ACACHE_EALIGN;
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_store_plan(read_slot, kv_offsets, src_pos, src_offsets, B, max_kv_per_req, w.stride,
-                                   (int32_t*)(ws + w.other), (int32_t*)(ws + w.counts), s);
-  if (e != hipSuccess) return status_of(e);
   StoreAttnArgs a;
   a.q = q;
   a.pool_k = pool->k;
@@ -551,6 +585,10 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
   a.scale = scale;
   a.out = out;
   a.lse = lse;
+  if ((st = limits_of(launch_attn_mfma_store(a, s, true)))) return st;
+  hipError_t e = launch_store_plan(read_slot, kv_offsets, src_pos, src_offsets, B, max_kv_per_req, w.stride,
+                                   (int32_t*)(ws + w.other), (int32_t*)(ws + w.counts), s);
+  if (e != hipSuccess) return status_of(e);
   return status_of(launch_attn_mfma_store(a, s));
 }
 

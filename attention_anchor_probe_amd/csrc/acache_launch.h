@@ -133,8 +133,12 @@ inline int gqa_pack(int n_q_heads, int n_kv_heads, int max_q) {
   const int G = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
   return (G > 1 && (max_q > 32 || (long long)G * max_q >= 128)) ? G : 0;
 }
-hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
-hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st);
+// The MFMA launches check the sizes their kernels index with 32 bits;
+// dry_run = true checks them (same return value) and launches nothing, so
+// that a call made of several launches can reject its arguments before it
+// enqueues anything.
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run = false);
+hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st, bool dry_run = false);
 
 // Store-then-attend, many-query MFMA path: request b's rows attend to
 // other_slots[b * other_stride .. + other_counts[b]) (pool slots) and to rows
@@ -165,7 +169,7 @@ struct StoreAttnArgs {
   void* out;
   float* lse;
 };
-hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st);
-hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st);
+hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool dry_run = false);
+hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_run = false);
 
 }  // namespace acache

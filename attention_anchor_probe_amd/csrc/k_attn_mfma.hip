@@ -1163,7 +1163,7 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
 
 bool mfma_supported(int dtype, int head_dim) { return dtype == ACACHE_BF16 && head_dim == D; }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   const int B = a.q_offsets ? a.B : 1;
   const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
   const bool split = G == 0 && a.max_q <= 32;
@@ -1197,13 +1197,14 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
+  if (dry_run) return hipSuccess;
   dim3 grid(8 * p.per_xcd), block(256);
   if (split) hipLaunchKernelGGL(attn_split_mfma, grid, block, 0, st, p);
   else hipLaunchKernelGGL(attn_rows_mfma, grid, block, 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool dry_run) {
   const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
   if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
   const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
@@ -1243,11 +1244,12 @@ hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st) {
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL(attn_store_rows_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st, bool dry_run) {
   if (a.max_q > 32) return hipErrorInvalidValue;
   AttnP p{};
   p.q = (const bf16_t*)a.q;
@@ -1277,11 +1279,12 @@ hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st) {
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL(attn_shared_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st) {
+hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_run) {
   ColP p;
   p.q = (const bf16_t*)a.q;
   p.pool_k = (const bf16_t*)a.pool_k;
@@ -1303,6 +1306,7 @@ hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st) {
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL(colmass_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }

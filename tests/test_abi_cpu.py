@@ -203,6 +203,25 @@ def test_store_attend_validation_and_workspace():
     assert sa(ws=FAKE + 4) == -9
 
 
+def test_size_limits_rejected_before_any_launch():
+    """A pool whose layers exceed the 32-bit byte offsets of the MFMA kernels
+    is rejected with ESHAPE by every call that would launch them, before the
+    call enqueues anything (its plan or scatter kernels included): on this
+    host without a GPU any launch would fail with EDEVICE instead."""
+    lib = Bd._lib()
+    big = pool(n_pages=1 << 20, n_kv_heads=8)          # 2^20 pages x 8 heads x 4 KiB = 32 GiB per layer
+    assert lib.acache_mapped_attention(ctypes.byref(big), FAKE, FAKE, 8, 8, FAKE, FAKE, 100, 1, 8, 0, 2, 0.1, FAKE,
+                                       None, None, 0, None) == -3
+    ws = ctypes.c_size_t()
+    assert lib.acache_mapped_attention_shared_workspace_bytes(ctypes.byref(big), 1, 8, 8, 8, 2, 100, 64,
+                                                              ctypes.byref(ws)) == 0
+    assert lib.acache_mapped_attention_shared(ctypes.byref(big), FAKE, FAKE, 8, 8, FAKE, FAKE, 100, FAKE, 0, 64, 1, 8,
+                                              0, 2, 0.1, FAKE, None, FAKE * 16, max(ws.value, 16), None) == -3
+    assert lib.acache_store_attend(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 8, 8, FAKE, FAKE,
+                                   100, 1, 8, 0, 2, 0.1, FAKE, None, FAKE * 16, 1 << 24, None) == -3
+    assert lib.acache_probe_attention(ctypes.byref(big), FAKE, 10, FAKE, 32, 8, 0, 2, 0.1, None, FAKE, None) == -3
+
+
 def _ws_query(lib, pl, B, n_q, mq, hq, nl, mkv, L):
     out = ctypes.c_size_t()
     assert lib.acache_mapped_attention_shared_workspace_bytes(ctypes.byref(pl), B, n_q, mq, hq, nl, mkv, L,
