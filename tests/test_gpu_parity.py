@@ -256,7 +256,7 @@ def test_mapped_attention_ragged(dtype, d):
 
 
 @pytest.mark.parametrize("hkv", [2, 4], ids=["g4-packed", "g2-shared-kernel"])
-@pytest.mark.parametrize("case", ["mixed", "no-affix", "all-private", "short", "many"])
+@pytest.mark.parametrize("case", ["mixed", "no-affix", "all-private", "short", "many", "wide"])
 def test_shared_affix_attention_seeded(case, hkv):
     """The shared-affix entry point on read tables that route a random part of
     the affix to the shared slots and the rest anywhere in the pool, with
@@ -264,8 +264,11 @@ def test_shared_affix_attention_seeded(case, hkv):
     and contexts (one shorter than the affix end, an empty one).  Its result
     is defined by the read table alone: same oracle as acache_mapped_attention.
     With 4 query heads per KV head a 32-row block fills a packed 128-row tile
-    and the call runs the single pass; with 2 it runs the shared-affix kernel."""
-    w = Workload(101, "sh", "bf16", 2, 8, hkv, 128, (("req", 40), ("affix", 333), ("gen", 64)), 7, 0.2,
+    and the call runs the single pass; with 2 it runs the shared-affix kernel
+    (four requests per workgroup: the "wide" case's 11 requests leave its
+    third group one request short)."""
+    nb = 11 if case == "wide" else 7
+    w = Workload(101, "sh", "bf16", 2, 8, hkv, 128, (("req", 40), ("affix", 333), ("gen", 64)), nb, 0.2,
                  page_order="random")
     K = A.acache_anchor_count(w.L, w.rate)
     lay = gen.make_layout(w, K, 5)
@@ -278,6 +281,9 @@ def test_shared_affix_attention_seeded(case, hkv):
     q_counts = [32, 0, 17, 32, 5, 1, 32]
     if case == "many":
         q_counts = [32] * 7
+    if case == "wide":
+        T += [437, 200, 437, 437]
+        q_counts += [32, 9, 0, 32]
     tables = []
     for b, t in enumerate(T):
         rs = rng.integers(0, nslot, t).astype(np.int32)
