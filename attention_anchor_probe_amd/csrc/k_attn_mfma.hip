@@ -6,7 +6,11 @@
 //   (Eq. 4 of "Affix Cache for Diffusion Large Language Models", Section 3.2)
 //   and the read-slot attention of Section 4.3 / Appendix C.1, in two shapes:
 //     attn_rows_mfma   a workgroup owns 128 query rows (32 per wave) and every
-//                      wave walks every key (probe, recompute-sized sets);
+//                      wave walks every key (probe, recompute-sized sets;
+//                      grouped query heads packed into the rows of a unit);
+//     attn_store_rows_mfma  the same over a request's other keys and then its
+//                      freshly recomputed rows, read from their source while
+//                      the same launch stores them (store-then-attend);
 //     attn_split_mfma  a workgroup owns 32 query rows and its four waves split
 //                      each 128-key tile into four 32-key slices; the partial
 //                      (max, sum, O) of the waves are merged at the end

@@ -3,6 +3,8 @@
 //     Diffusion Large Language Models", Section 3.2),
 //   * the write-side recomputation map and the per-request read-slot map
 //     (Section 4.1 dual mapping, Section 4.2 admission-time preparation),
+//   * the plans of the shared-affix and store-then-attend attentions (each
+//     request's read list split by where its keys are read from),
 //   * decode-block destination slots (Section 4.3, block decoding),
 //   * the private scatter of recomputed K/V rows (Section 4.3 and
 //     Appendix C.1: new KV is stored through the write-side map before the
