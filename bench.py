@@ -351,18 +351,33 @@ def work_model(w, K):
                 block_bytes=2 * nb * kv_bytes_per_pos)
 
 
+TRAFFIC_SOURCES = ("k_attn_mfma.hip", "k_tables.hip")   # the sources of the counted kernels
+
+
+def code_digest(path):
+    """sha256 of a kernel source without its comments and white space: it
+    changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", "", txt)
+    return hashlib.sha256(re.sub(r"\s+", "", txt).encode()).hexdigest()
+
+
 def measured_traffic(workload_name):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (scaled by the counters' reading of a 1 GiB device copy), or None for
-    a kernel whose source changed since the counters were taken."""
-    import hashlib
+    runs (scaled by the counters' reading of a 1 GiB device copy), or {} (no
+    figure) when the code of a counted kernel changed since the counters were
+    taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload_name}.json")
     if not os.path.exists(path):
         return {}
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "attention_anchor_probe_amd", "csrc", "k_attn_mfma.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"].get("k_attn_mfma.hip"):
-        return {}
+    digests = rec.get("code_sha256", {})
+    for f in TRAFFIC_SOURCES:
+        if code_digest(os.path.join(ROOT, "attention_anchor_probe_amd", "csrc", f)) != digests.get(f):
+            return {}
     return {k: v["hbm_bytes"] for k, v in rec["kernels"].items()}
 
 
