@@ -592,7 +592,9 @@ def test_probe_full_normaliser_chain(idx):
     probe attention over the affix, read-slot attention of the same rows over
     their own non-affix keys, LSE merge, column mass with the merged LSE.
     O, LSE and scores against the oracle's one-softmax formulation, and the
-    anchor sets under this reading against the oracle's."""
+    anchor sets under this reading against the oracle's.  Then the same
+    normaliser in one pass (each request's rows over its affix slots followed
+    by its own slots) against the same oracle values."""
     name, w = SMALL[idx]
     K = A.acache_anchor_count(w.L, w.rate)
     lay = gen.make_layout(w, K, 9)
@@ -623,9 +625,11 @@ def test_probe_full_normaliser_chain(idx):
     torch.cuda.synchronize()
     fp32 = w.dtype == "f32"
     s_ref = np.zeros((w.batch, w.L))
+    refs = {}
     for n in range(w.n_layers):
         of, lf, sf = O.probe_layer_full(hq[n], hk[n], hv[n], lay.shared_slots, lay.row_offsets, na, na_off,
                                         w.page_size, w.n_kv_heads, lay.masked_rows, lay.masked_offsets, scale)
+        refs[n] = (of, lf)
         s_ref += sf
         got = np_of(o_aff[n]).astype(np.float64) if fp32 else o_aff[n].float().cpu().numpy()
         if fp32:
@@ -646,6 +650,32 @@ def test_probe_full_normaliser_chain(idx):
     for b in range(w.batch):
         ok, _ = anchors_match(s_ref[b], an.cpu().numpy()[b], K, w.affix_l)
         assert ok
+    # the same normaliser in one pass: each request's rows attend to the
+    # affix slots followed by their own slots (one softmax, no merge)
+    one, one_off = [], [0]
+    for b in range(w.batch):
+        one += list(lay.shared_slots) + list(na[na_off[b]:na_off[b + 1]])
+        one_off.append(len(one))
+    o1 = torch.empty_like(q)
+    l1 = torch.empty_like(lse_aff)
+    A.acache_mapped_attention(k, v, q, i32(lay.row_offsets), i32(np.array(one, np.int32)),
+                              i32(np.array(one_off, np.int32)), o1, lse=l1, max_q_per_req=max_p,
+                              max_kv_per_req=w.L + max_p)
+    s1 = torch.zeros((w.batch, w.L), device=DEV)
+    A.acache_probe_column_mass(k, v, q, i32(lay.masked_rows), i32(lay.masked_offsets), i32(lay.shared_slots),
+                               l1, s1, max_masked=w.m)
+    torch.cuda.synchronize()
+    for n in range(w.n_layers):
+        of, lf = refs[n]
+        got = np_of(o1[n]).astype(np.float64) if fp32 else o1[n].float().cpu().numpy()
+        if fp32:
+            assert np.abs(got - of).max() <= 1e-5
+        else:
+            ok, st = bf16_close(got, of)
+            assert ok, f"one-pass full-normaliser O layer {n}: {st}"
+        np.testing.assert_allclose(l1[n].cpu().numpy(), lf, atol=1e-4)
+    s1 = s1.cpu().numpy().astype(np.float64)
+    assert (np.abs(s1 - s_ref)[big] / s_ref[big]).max() <= (1e-5 if fp32 else 1e-3)
 
 
 @pytest.mark.parametrize("wl", ["small-f32", "small-bf16", "dream-gqa-L2048"])
