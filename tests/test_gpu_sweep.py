@@ -1,6 +1,12 @@
-"""Seeded sweep of small random shapes through the three read-slot attention
-calls (single pass, shared affix, store-then-attend) against the oracle
-(Section 4.3, Appendix C.1): head dims 16-128, grouped query heads
+"""Seeded sweeps of small random shapes against the oracle.
+
+The probe and the maps (Section 3.2 Eq. 4-6, Section 4.1): probe O_aff, LSE
+and scores over 1-3 layers, the Top-K on the library's own scores against a
+sort of the same scores (bit-exact), and both maps against the oracle's maps
+of those anchors (bit-exact).
+
+The three read-slot attention calls (single pass, shared affix,
+store-then-attend; Section 4.3, Appendix C.1): head dims 16-128, grouped query heads
 (G = 1..5), page sizes 4-32, bf16 and fp32 pools, ragged query blocks (empty
 ones included), contexts of 0 or 1 key, affixes that start anywhere, read
 tables with a random share of the affix routed to the shared slots.  Each
@@ -134,3 +140,75 @@ def test_read_slot_attention_sweep(seed):
     O.scatter(kp, vp, skh, svh, np.array(src_slot, np.int32), w.page_size)
     assert np.array_equal(np_of(k), kp) and np.array_equal(np_of(v), vp), "pool after store-then-attend"
     check(out, lse, kp, vp, "store-then-attend")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_probe_and_maps_sweep(seed):
+    rng = np.random.default_rng(5000 + seed)
+    dtype = "f32" if seed % 5 == 4 else "bf16"
+    d = int(rng.choice([16, 32, 64, 128])) if dtype == "f32" or seed % 3 == 0 else 128
+    hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 7]))
+    ps = int(rng.choice([4, 8, 16, 32]))
+    L = int(rng.integers(1, 400))
+    pre, mid = int(rng.integers(0, 50)), int(rng.integers(0, 30))
+    m = int(rng.integers(1, 90))
+    segs = ([("req", pre)] if pre else []) + [("affix", L)] + ([("req", mid)] if mid else []) + [("gen", m)]
+    if rng.random() < 0.3:   # affix as a suffix
+        segs = ([("req", pre)] if pre else []) + [("gen", m), ("affix", L)]
+    w = Workload(300 + seed, f"psweep{seed}", dtype, int(rng.integers(1, 4)), G * hkv, hkv, d, tuple(segs),
+                 int(rng.integers(1, 7)), float(rng.choice([0.0, 0.1, 0.3, 0.5, 1.0])), page_size=ps,
+                 page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    assert K == O.anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, seed)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=seed)
+    q = gen.make_probe_q(w, lay, device=DEV, seed=seed)
+    torch.cuda.synchronize()
+    kh, vh, qh = map(np_of, (k, v, q))
+    scale = 1 / math.sqrt(w.head_dim)
+    scores = torch.zeros((w.batch, w.L), device=DEV)
+    o_aff = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=DEV)
+    A.acache_probe_scores(k, v, q, i32(lay.masked_rows), i32(lay.masked_offsets), i32(lay.shared_slots), scores,
+                          max_masked=w.m, o_aff=o_aff, lse_aff=lse)
+    n_rc = int(lay.rc_offsets[-1])
+    anchors = torch.empty((w.batch, K), dtype=torch.int32, device=DEV)
+    read_slot = torch.empty(int(lay.kv_offsets[-1]), dtype=torch.int32, device=DEV)
+    rc_pos = torch.empty(max(n_rc, 1), dtype=torch.int32, device=DEV)
+    rc_slot = torch.empty_like(rc_pos)
+    keep = [i32(x) for x in (lay.seq_len, lay.shared_slots, lay.private_pages, lay.private_page_offsets,
+                             lay.kv_offsets, lay.rc_offsets)]
+    maps = A.map_args(w.batch, w.affix_l, w.L, K, w.page_size, w.T, *keep, read_slot, rc_pos, rc_slot)
+    A.acache_topk_anchors(scores, K, w.affix_l, anchors, maps)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()
+    s_ref = np.zeros((w.batch, w.L))
+    for n in range(w.n_layers):
+        o_ref, l_ref, s_n = O.probe_layer(qh[n], kh[n], vh[n], lay.shared_slots, w.page_size, w.n_kv_heads,
+                                          lay.masked_rows, lay.masked_offsets, scale)
+        s_ref += s_n
+        o = np_of(o_aff[n]).astype(np.float64) if dtype == "f32" else o_aff[n].float().cpu().numpy()
+        if dtype == "f32":
+            assert np.abs(o - o_ref).max() <= 1e-5
+        else:
+            ok, st = bf16_close(o, o_ref)
+            assert ok, (n, st)
+        np.testing.assert_allclose(lse[n].cpu().numpy(), l_ref, atol=1e-4)
+    big = s_ref >= 1e-6 * s_ref.max()
+    assert (np.abs(s_gpu - s_ref)[big] / s_ref[big]).max(initial=0.0) <= (1e-5 if dtype == "f32" else 1e-3)
+    np.testing.assert_allclose(s_gpu.sum(axis=1), w.n_layers * w.n_q_heads * np.diff(lay.masked_offsets),
+                               rtol=1e-4)
+    # Top-K on the library's own scores: the same set and order as a sort of
+    # those scores (ties to the lower offset), bit for bit
+    an = anchors.cpu().numpy()
+    rd, rp, rs = [], [], []
+    for b in range(w.batch):
+        want = O.topk_anchors(s_gpu[b].astype(np.float64), K, w.affix_l)
+        assert np.array_equal(an[b], want), f"request {b}"
+        pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+        r_, p_, s_ = O.build_maps(an[b], int(lay.seq_len[b]), w.affix_l, w.L, lay.shared_slots, pp, w.page_size)
+        rd.append(r_); rp.append(p_); rs.append(s_)
+    assert np.array_equal(read_slot.cpu().numpy(), np.concatenate(rd))
+    assert np.array_equal(rc_pos.cpu().numpy()[:n_rc], np.concatenate(rp))
+    assert np.array_equal(rc_slot.cpu().numpy()[:n_rc], np.concatenate(rs))
