@@ -1048,11 +1048,17 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
 // Column mass of the masked rows.  A workgroup owns 256 affix keys (64 per
 // wave, held as two B-operand tiles in registers) of one (layer, query head)
 // and streams every request's masked rows through LDS in tiles of 32.  The
-// tiles of all requests are walked as one list; row indices are loaded two
-// tiles ahead and Q rows / LSE values one tile ahead of their use.
+// tiles of all requests are walked as one list.  Q rows go straight from
+// global memory to LDS (direct-to-LDS loads, the same swizzled 256-byte row
+// layout as the K tiles of the attention), two stages deep: right after the
+// barrier of iteration t the loads of tile t+2 start, and they land during
+// the iteration.  The loop is software pipelined: while a wave takes the
+// exponentials of tile t, it computes the scores of tile t+1.  Each score
+// accumulator starts at -LSE/scale of its row, so that the weight is
+// exp2(c2 * accumulator).
 __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * KS];
-  __shared__ __attribute__((aligned(16))) float lse2[32];
+  __shared__ __attribute__((aligned(1024))) char Qs[2][32 * ROWB];
+  __shared__ __attribute__((aligned(16))) float lse2[2][32];
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
   const int kblk = unit % p.key_blocks;
@@ -1075,81 +1081,124 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     for (int c = 0; c < 8; ++c) kf[nt][c] = as_bf16x8(ld16(kp + c * 16));
   }
 
+  // request offsets are the same for every lane: read them as scalars
+  const __attribute__((address_space(4))) int32_t* moff =
+      (const __attribute__((address_space(4))) int32_t*)p.masked_offsets;
   float* part = p.partial + ((size_t)n * p.n_q_heads + h) * p.B * p.L;
   const int j0 = kw + l32, j1 = kw + 32 + l32;
   // requests without masked rows contribute zero
   for (int b = 0; b < p.B; ++b)
-    if (p.masked_offsets[b + 1] == p.masked_offsets[b] && g2 == 0) {
+    if (moff[b + 1] == moff[b] && g2 == 0) {
       if (j0 < p.L) part[(size_t)b * p.L + j0] = 0.f;
       if (j1 < p.L) part[(size_t)b * p.L + j1] = 0.f;
     }
 
-  // tile iterator over (request, first masked row) of all non-empty requests
+  // tile iterator over (request, first masked row) of all non-empty requests;
+  // past the last request it points at row 0 of the masked list (which
+  // exists whenever a tile does), so that loads issued ahead stay in bounds
   struct It { int b, r0, m1; };
   auto first_from = [&](int b) -> It {
-    while (b < p.B && p.masked_offsets[b + 1] == p.masked_offsets[b]) ++b;
-    if (b >= p.B) return It{p.B, 0, 0};
-    return It{b, p.masked_offsets[b], p.masked_offsets[b + 1]};
+    while (b < p.B && moff[b + 1] == moff[b]) ++b;
+    if (b >= p.B) return It{p.B, 0, 1};
+    return It{b, moff[b], moff[b + 1]};
   };
   auto next = [&](It t) -> It {
     if (t.b >= p.B) return t;
     if (t.r0 + 32 < t.m1) return It{t.b, t.r0 + 32, t.m1};
     return first_from(t.b + 1);
   };
-
-  const int rr0 = tid >> 4, rr1 = 16 + (tid >> 4), dc = tid & 15;
-  int ri0 = 0, ri1 = 0, ril = 0;        // masked-row indices of a tile
-  u32x4 q0 = {0, 0, 0, 0}, q1 = {0, 0, 0, 0};
-  float lv = INFINITY;
-  auto rows_load = [&](It t) {
-    ri0 = p.masked_rows[min(t.r0 + rr0, t.m1 - 1)];
-    ri1 = p.masked_rows[min(t.r0 + rr1, t.m1 - 1)];
-    if (tid < 32) ril = p.masked_rows[min(t.r0 + tid, t.m1 - 1)];
-  };
-  auto q_load = [&](It t) {
-    const size_t base = (size_t)n * p.n_rows;
-    q0 = ld16(p.q + ((base + ri0) * p.n_q_heads + h) * D + dc * 8);
-    q1 = ld16(p.q + ((base + ri1) * p.n_q_heads + h) * D + dc * 8);
-    if (tid < 32) lv = t.r0 + tid < t.m1 ? p.lse[(base + ril) * p.n_q_heads + h] * kLog2e : INFINITY;
-  };
-
   It t0 = first_from(0);
-  It t1 = next(t0);
-  if (t0.b < p.B) {
-    rows_load(t0);
-    q_load(t0);
-    if (t1.b < p.B) rows_load(t1);
-  }
-  float acc0 = 0.f, acc1 = 0.f;
-  while (t0.b < p.B) {
-    const It t2 = next(t1);
-    __syncthreads();
-    // rows past the request's end carry LSE = +inf, so they add exp2(-inf) = 0
-    *(u32x4*)(Qs + rr0 * KS + dc * 8) = q0;
-    *(u32x4*)(Qs + rr1 * KS + dc * 8) = q1;
-    if (tid < 32) lse2[tid] = lv;
-    __syncthreads();
-    if (t1.b < p.B) {
-      q_load(t1);
-      if (t2.b < p.B) rows_load(t2);
-    }
-    bf16x8 qa[8];
-    const bf16_t* qp = Qs + l32 * KS + g2 * 8;
+  if (t0.b >= p.B) return;  // no masked rows anywhere (uniform over the workgroup)
+
+  // Direct-to-LDS loads: instruction i of wave w fills tile rows 8w+4i ..
+  // 8w+4i+3, lane/16 picking the row and lane%16 the LDS chunk, which holds
+  // the row's global chunk kswz(row, lane%16).
+  const int ra = 8 * wave + (lane >> 4);  // tile rows this lane moves: ra, ra + 4
+  const uint32_t gchunk0 = kswz(ra, lane & 15) * 16, gchunk1 = kswz(ra + 4, lane & 15) * 16;
+  const char* qhead = (const char*)(p.q + ((size_t)n * p.n_rows * p.n_q_heads + h) * D);
+  const size_t qrow_bytes = (size_t)p.n_q_heads * D * sizeof(bf16_t);
+  const uint32_t lds_q = lds_addr(&Qs[0][0]) + 8 * wave * ROWB;
+  const float neg_inv_scale = -kLog2e / p.c2;
+  // masked-row indices of a tile: the two rows this lane moves, and row
+  // lane%32 (whose LSE lanes 0..31 stage)
+  struct RowIdx { int ra, rb, rl; };
+  auto rows_load = [&](It t) -> RowIdx {
+    RowIdx ix;
+    ix.ra = p.masked_rows[min(t.r0 + ra, t.m1 - 1)];
+    ix.rb = p.masked_rows[min(t.r0 + ra + 4, t.m1 - 1)];
+    ix.rl = p.masked_rows[min(t.r0 + l32, t.m1 - 1)];
+    return ix;
+  };
+  auto dma_q = [&](int stage, const RowIdx& ix) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_q + stage * (32 * ROWB));
+    dma16(qhead + (size_t)ix.ra * qrow_bytes + gchunk0, dst);
+    dma16(qhead + (size_t)ix.rb * qrow_bytes + gchunk1, dst + 4 * ROWB);
+  };
+  // every lane loads the LSE of row lane%32; lanes 0..31 store it, an
+  // iteration later (rows past the request's end start at -inf, so they add
+  // exp2(-inf) = 0)
+  auto lse_load = [&](const RowIdx& ix) { return p.lse[((size_t)n * p.n_rows + ix.rl) * p.n_q_heads + h]; };
+  auto lse_store = [&](int stage, It t, float l) {
+    if (tid < 32) lse2[stage][tid] = t.r0 + tid < t.m1 ? l * neg_inv_scale : -INFINITY;
+  };
+  // scores of the tile in stage st, from accumulators that start at its
+  // rows' -LSE/scale
+  uint32_t qrd[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qa[c] = as_bf16x8(*(const u32x4*)(qp + c * 16));
-    float lrow[16];
+  for (int c = 0; c < 8; ++c) qrd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
+  auto scores = [&](f32x16* s, int st) {
+    const char* qs = &Qs[st][0];
+    f32x16 init;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lrow[i] = lse2[8 * (i >> 2) + 4 * g2 + (i & 3)];
-    f32x16 s0 = {}, s1 = {};
+    for (int i = 0; i < 16; ++i) init[i] = lse2[st][8 * (i >> 2) + 4 * g2 + (i & 3)];
+    s[0] = init;
+    s[1] = init;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      s0 = mfma(qa[c], kf[0][c], s0);
-      s1 = mfma(qa[c], kf[1][c], s1);
+      const bf16x8 qa = as_bf16x8(*(const u32x4*)(qs + qrd[c]));
+      s[0] = mfma(qa, kf[0][c], s[0]);
+      s[1] = mfma(qa, kf[1][c], s[1]);
     }
+  };
+
+  // prologue: tiles t0 and t1 loading into stages 0 and 1, t1's LSE in
+  // registers, t2's row indices
+  It t1 = next(t0), t2 = next(t1), t3 = next(t2);
+  {
+    const RowIdx i0 = rows_load(t0);
+    dma_q(0, i0);
+    lse_store(0, t0, lse_load(i0));
+  }
+  RowIdx in = rows_load(t1);
+  dma_q(1, in);
+  float lq = lse_load(in);
+  in = rows_load(t2);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tile t0 (and t1) in LDS, t2's indices in registers
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(sa, 0);
+  int st = 0;  // stage of tile t0
+  float acc0 = 0.f, acc1 = 0.f;
+
+  // one tile: sc holds the scores of t0, sn receives those of t1
+  auto step = [&](f32x16* sc, f32x16* sn) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's loads of t1 (and t2's indices) landed
+    lse_store(st ^ 1, t1, lq);
+    __syncthreads();  // t1 is in stage st^1 for every wave; no wave still reads stage st
+    // tile t2 into stage st, and the indices of t3, while this iteration computes
+    if (t2.b < p.B) {
+      dma_q(st, in);
+      lq = lse_load(in);
+    }
+    const It t4 = next(t3);
+    in = rows_load(t3);
+    // past the last tile the scores read a stale stage and are never used;
+    // computing them keeps this block branch-free
+    scores(sn, st ^ 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc0 += fast_exp2(fmaf(s0[i], p.c2, -lrow[i]));
-      acc1 += fast_exp2(fmaf(s1[i], p.c2, -lrow[i]));
+      acc0 += fast_exp2(sc[0][i] * p.c2);
+      acc1 += fast_exp2(sc[1][i] * p.c2);
     }
     if (t1.b != t0.b) {  // last tile of this request: write its partial column masses
       const float a0 = half_sum(acc0);
@@ -1162,6 +1211,15 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     }
     t0 = t1;
     t1 = t2;
+    t2 = t3;
+    t3 = t4;
+    st ^= 1;
+  };
+  while (true) {
+    step(sa, sb);
+    if (t0.b >= p.B) break;
+    step(sb, sa);
+    if (t0.b >= p.B) break;
   }
 }
 
