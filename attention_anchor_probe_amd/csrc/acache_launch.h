@@ -119,7 +119,7 @@ hipError_t launch_hkvd(const void* pool_k, const void* pool_v, const PoolGeom& g
 
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_colmass_generic(const ColmassArgs& a, int dtype, hipStream_t st);
-hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int L, float* scores, hipStream_t st);
+hipError_t launch_colmass_reduce(const float* partial, int n_rows, int B, int L, float* scores, hipStream_t st);
 
 // bf16, head_dim 128, MFMA kernels (k_attn_mfma.hip)
 bool mfma_supported(int dtype, int head_dim);

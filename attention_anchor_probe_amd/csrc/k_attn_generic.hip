@@ -10,8 +10,9 @@
 //   colmass_generic  : per-key Eq. (4) weights of the masked rows, summed over
 //                      query heads and rows into one partial per (layer,
 //                      request, key)  (Eq. 5).
-//   colmass_reduce   : scores[b][j] += sum over layers of the partials, in
-//                      ascending layer order (deterministic).
+//   colmass_reduce   : scores[b][j] += sum of the partials over their first
+//                      index (layers, or layers x query heads), in a fixed
+//                      order (deterministic).
 #include "acache_dev.h"
 #include "acache_launch.h"
 
@@ -123,13 +124,33 @@ __global__ __launch_bounds__(64) void colmass_generic(
   partial[((size_t)n * B + b) * L + j] = acc;
 }
 
-__global__ __launch_bounds__(256) void colmass_reduce(const float* __restrict__ partial, int n_layers, int BL,
-                                                      float* __restrict__ scores) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= BL) return;
-  float acc = 0.f;
-  for (int n = 0; n < n_layers; ++n) acc += partial[(size_t)n * BL + t];
-  scores[t] += acc;
+// A workgroup owns 32 consecutive (request, key) columns; its eight row
+// groups each sum every eighth partial row (four independent accumulators,
+// so that each thread keeps four loads in flight), and the group sums are
+// added in group order.  The order is fixed, so the result is deterministic.
+constexpr int kRedCols = 32, kRedGroups = 8;
+__global__ __launch_bounds__(kRedCols * kRedGroups) void colmass_reduce(const float* __restrict__ partial,
+                                                                        int n_rows, int BL,
+                                                                        float* __restrict__ scores) {
+  __shared__ float part[kRedGroups][kRedCols];
+  const int c = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
+  const int t = blockIdx.x * kRedCols + c;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (t < BL) {
+    int n = grp;
+    for (; n + 3 * kRedGroups < n_rows; n += 4 * kRedGroups)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += partial[(size_t)(n + u * kRedGroups) * BL + t];
+    for (; n < n_rows; n += kRedGroups) acc[0] += partial[(size_t)n * BL + t];
+  }
+  part[grp][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (grp == 0 && t < BL) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRedGroups; ++k) sum += part[k][c];
+    scores[t] += sum;
+  }
 }
 
 template <typename T>
@@ -176,10 +197,11 @@ hipError_t launch_colmass_generic(const ColmassArgs& a, int dtype, hipStream_t s
   return dtype == ACACHE_F32 ? colmass_generic_dispatch<float>(a, st) : colmass_generic_dispatch<bf16_t>(a, st);
 }
 
-hipError_t launch_colmass_reduce(const float* partial, int n_layers, int B, int L, float* scores, hipStream_t st) {
+hipError_t launch_colmass_reduce(const float* partial, int n_rows, int B, int L, float* scores, hipStream_t st) {
   const int BL = B * L;
   if (BL == 0) return hipSuccess;
-  hipLaunchKernelGGL(colmass_reduce, dim3((BL + 255) / 256), dim3(256), 0, st, partial, n_layers, BL, scores);
+  hipLaunchKernelGGL(colmass_reduce, dim3((BL + kRedCols - 1) / kRedCols), dim3(kRedCols * kRedGroups), 0, st,
+                     partial, n_rows, BL, scores);
   return hipGetLastError();
 }
 
