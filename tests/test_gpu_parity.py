@@ -518,6 +518,51 @@ def test_probe_is_deterministic_and_accumulates():
     np.testing.assert_allclose(s3.cpu().numpy(), s1.cpu().numpy(), rtol=1e-5)
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 4, 2), ("f32", 64, 3, 3)])
+def test_column_mass_ragged_masked_sets(dtype, d, hq, hkv):
+    """Eq. (4)-(5) with ragged masked sets per request: none, one row, exactly
+    one 32-row tile, a ragged tail over several tiles, a request with none
+    between two that have rows.  scores accumulate (+=): a request without
+    masked rows keeps its initial value.  A second call in which no request
+    has a masked row leaves scores unchanged."""
+    w = Workload(121, "ragged-mask", dtype, 2, hq, hkv, d, (("affix", 300), ("req", 20), ("gen", 70)), 7, 0.2,
+                 page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, 4)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=4)
+    q = gen.make_probe_q(w, lay, device=DEV, seed=4)
+    counts = [0, 1, 32, 0, 70, 45, 0]
+    rng = np.random.default_rng(4)
+    rows, off = [], [0]
+    for b, c in enumerate(counts):
+        r0, r1 = int(lay.row_offsets[b]), int(lay.row_offsets[b + 1])
+        rows += sorted(rng.choice(np.arange(r0, r1), size=c, replace=False).tolist())
+        off.append(len(rows))
+    rows, off = np.array(rows, np.int32), np.array(off, np.int32)
+    scores = torch.full((w.batch, w.L), 0.5, device=DEV)
+    A.acache_probe_scores(k, v, q, i32(rows), i32(off), i32(lay.shared_slots), scores, max_masked=max(counts))
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    kh, vh, qh = np_of(k), np_of(v), np_of(q)
+    ref = np.full((w.batch, w.L), 0.5)
+    for n in range(w.n_layers):
+        ref += O.probe_layer(qh[n], kh[n], vh[n], lay.shared_slots, w.page_size, w.n_kv_heads, rows, off,
+                             1 / math.sqrt(d), want_out=False)[2]
+    for b, c in enumerate(counts):
+        if c == 0:
+            assert (got[b] == 0.5).all(), f"request {b} has no masked rows"
+    rel = np.abs(got - ref) / ref
+    assert rel.max() <= (1e-5 if dtype == "f32" else 1e-3), rel.max()
+    np.testing.assert_allclose(got.sum(axis=1), 0.5 * w.L + w.n_layers * hq * np.array(counts), rtol=1e-4)
+    # no masked rows anywhere: nothing is added
+    before = scores.clone()
+    A.acache_probe_scores(k, v, q, torch.empty(0, dtype=torch.int32, device=DEV),
+                          torch.zeros(w.batch + 1, dtype=torch.int32, device=DEV), i32(lay.shared_slots), scores,
+                          max_masked=0)
+    torch.cuda.synchronize()
+    assert torch.equal(scores, before)
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_dropna_attention(idx):
     """DropNA (Section 5.3): the recompute map doubles as the read table with
