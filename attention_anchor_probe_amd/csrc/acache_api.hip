@@ -544,7 +544,11 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
   if (n_src > 0 && (!k_src || !v_src || !src_pos || !src_slot || !src_offsets)) return ACACHE_EINVAL;
   if (n_src > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
   const StoreWs w = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req);
-  if (!w.fused || B == 0 || n_q == 0 || n_layers == 0) {
+  // With more than three query heads per KV head the rows to store are few
+  // beside the attention, and splitting each key list in two costs a partial
+  // tile per unit: there the two calls measured faster than one.
+  const bool fused = w.fused && n_q_heads <= 3 * pool->n_kv_heads;
+  if (!fused || B == 0 || n_q == 0 || n_layers == 0) {
     // the definition itself: the scatter, then the attention through
     // read_slot (the attention's arguments are checked before the scatter)
     hipStream_t s = (hipStream_t)stream;

@@ -129,12 +129,22 @@ class Setup:
                                          max_kv_per_req=w.T, workspace=self.ws_map)
         ev[6].record()
 
-    def recompute_ms(self, reps):
+    def extra_layers(self):
+        """Layers the recompute-phase timings run on: all of them when their
+        queries and outputs fit in half of the free device memory beside the
+        step's buffers, else the first that do (the L=16384 workload)."""
+        w = self.w
+        per_layer = 2 * self.n_rc * w.n_q_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
+        free, _ = torch.cuda.mem_get_info()
+        return max(1, min(w.n_layers, int(0.5 * free) // per_layer))
+
+    def recompute_ms(self, reps, nl):
         """Recompute-phase read-slot attention (Section 4.3): queries only for
         every request's recomputed rows (anchors and request positions),
-        keys and values through the read-slot map; timed on its own."""
+        keys and values through the read-slot map; layers 0 .. nl-1, timed on
+        its own."""
         w = self.w
-        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads)
+        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads, layers=range(nl))
         orc = torch.empty_like(qr)
         max_r = int(np.diff(self.lay.rc_offsets).max())
         rc_off = self._keep[5]
@@ -150,22 +160,23 @@ class Setup:
         del qr, orc
         return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
-    def store_attend_ms(self, reps):
+    def store_attend_ms(self, reps, nl):
         """The admission's store-then-attend in one call (Section 4.3): the
         recomputed K/V rows of every request are stored to their private slots
         and the recompute-phase queries attend through the read-slot map,
-        reading those rows from the source; timed on its own."""
+        reading those rows from the source; layers 0 .. nl-1, timed on its
+        own."""
         w = self.w
-        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads)
+        qr = gen.make_rows(w, self.n_rc, gen.S_QRC, device=self.dev, heads=w.n_q_heads, layers=range(nl))
         orc = torch.empty_like(qr)
         max_r = int(np.diff(self.lay.rc_offsets).max())
         rc_off = self._keep[5]
         nb = A.acache_store_attend_workspace_bytes(self.k, self.v, B=w.batch, max_q_per_req=max_r,
                                                    max_kv_per_req=w.T)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.dev)
-        run = lambda: A.acache_store_attend(self.k, self.v, self.src_k, self.src_v, self.rc_pos, self.rc_slot, rc_off,
-                                            qr, rc_off, self.read_slot, self.kv_offsets, orc, max_q_per_req=max_r,
-                                            max_kv_per_req=w.T, workspace=ws)
+        run = lambda: A.acache_store_attend(self.k, self.v, self.src_k[:nl], self.src_v[:nl], self.rc_pos,
+                                            self.rc_slot, rc_off, qr, rc_off, self.read_slot, self.kv_offsets, orc,
+                                            max_q_per_req=max_r, max_kv_per_req=w.T, workspace=ws)
         run()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record()
@@ -254,13 +265,19 @@ class Setup:
     def hkvd_ms(self, reps):
         """The CacheBlend-style HKVD selector scores (Appendix B.5) of every
         request's affix tokens over all layers, on synthetic full-prompt K/V
-        of the same shape; timed on its own.  Returns (ms, algorithmic GB)."""
+        of the same shape; timed on its own.  The full-prompt K/V of the first
+        nb requests that fit in half of the free device memory are timed (all
+        of them unless the workload is the L=16384 one) and the time scaled to
+        every request.  Returns (ms, algorithmic GB, nb)."""
         w = self.w
+        per_req = 2 * w.n_layers * w.L * w.n_kv_heads * w.head_dim * 2
+        free, _ = torch.cuda.mem_get_info()
+        nb = max(1, min(w.batch, int(0.5 * free) // per_req))
         g = torch.Generator(device=self.dev).manual_seed(5)
-        shape = (w.n_layers, w.batch, w.L, w.n_kv_heads, w.head_dim)
+        shape = (w.n_layers, nb, w.L, w.n_kv_heads, w.head_dim)
         kf = torch.randn(shape, generator=g, device=self.dev, dtype=torch.bfloat16)
         vf = torch.randn(shape, generator=g, device=self.dev, dtype=torch.bfloat16)
-        sc = torch.zeros((w.batch, w.L), device=self.dev)
+        sc = torch.zeros((nb, w.L), device=self.dev)
         A.acache_hkvd_scores(self.k, self.v, self.shared_slots, kf, vf, sc)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record()
@@ -268,9 +285,10 @@ class Setup:
             A.acache_hkvd_scores(self.k, self.v, self.shared_slots, kf, vf, sc)
             ev[i + 1].record()
         torch.cuda.synchronize()
-        gb = (kf.numel() + vf.numel()) * 2 / 1e9 + 2 * w.L * w.n_layers * w.n_kv_heads * w.head_dim * 2 / 1e9
+        # every request's full-prompt K/V once, and the shared affix K/V once
+        gb = (per_req * w.batch + 2 * w.L * w.n_layers * w.n_kv_heads * w.head_dim * 2) / 1e9
         del kf, vf, sc
-        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), gb
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * w.batch / nb, gb, nb
 
     def probe_single_request(self, reps):
         """The probe of one request alone at the same shapes (its non-affix
@@ -548,12 +566,14 @@ def main():
         evs[i][Setup.STAGES.index(name) + 1]) for i in range(args.steps)]))
     if not args.steps_only:
         single_ms = S.single_pass_ms(max(3, args.steps // 2))
-        rc_ms = S.recompute_ms(3)
-        sa_ms = S.store_attend_ms(3)
+        nl = S.extra_layers()
+        rc_ms = S.recompute_ms(3, nl)
+        sa_ms = S.store_attend_ms(3, nl)
+        lf = w.n_layers / nl   # the recompute timings scale to all layers
         dropna_ms = S.dropna_ms(max(3, args.steps // 2))
         progress("single-pass, recompute, store-then-attend and DropNA timings done")
         fn_ms, fn_overlap, fn_one_ms = S.full_normaliser()
-        hk_ms, hk_gb = S.hkvd_ms(3)
+        hk_ms, hk_gb, hk_nb = S.hkvd_ms(3)
         progress("full-context normaliser and HKVD timings done")
         single_req = S.probe_single_request(max(3, args.steps // 2))
         cold_warm = S.mapped_cold_warm(max(5, args.steps))
@@ -562,16 +582,18 @@ def main():
             "probe_single_request": single_req,
             "mapped_attention_cold_warm": cold_warm,
             "mapped_attention_single_pass_ms": single_ms,
-            "recompute_attention_ms": rc_ms,
-            "recompute_attention_tflops": work_model(w, S.K)["recompute_flops"] / (rc_ms * 1e-3) / 1e12,
-            "store_then_attend": {"one_call_ms": sa_ms,
-                                  "scatter_then_attention_ms": stage_mean("admission_scatter") + rc_ms,
-                                  "tflops": work_model(w, S.K)["recompute_flops"] / (sa_ms * 1e-3) / 1e12},
+            "recompute_layers_timed": nl,
+            "recompute_attention_ms": rc_ms * lf,
+            "recompute_attention_tflops": work_model(w, S.K)["recompute_flops"] / lf / (rc_ms * 1e-3) / 1e12,
+            "store_then_attend": {"one_call_ms": sa_ms * lf,
+                                  "scatter_then_attention_ms": stage_mean("admission_scatter") + rc_ms * lf,
+                                  "tflops": work_model(w, S.K)["recompute_flops"] / lf / (sa_ms * 1e-3) / 1e12},
             "dropna_mapped_attention_ms": dropna_ms,
             "full_normaliser": {"extra_ms": fn_ms, "anchor_overlap_with_affix_only": fn_overlap,
                                 "one_pass_ms": fn_one_ms,
                                 "one_pass_extra_ms": fn_one_ms - stage_mean("probe_attention")},
-            "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3)},
+            "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3),
+                              "requests_timed": hk_nb},
         }
     fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
     stage_t = {name: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
