@@ -370,9 +370,9 @@ class Setup:
 
 def work_model(w, K):
     """Algorithmic FLOPs and bytes of each stage (what the method must compute
-    or move; unique bytes, bf16 = 2 B)."""
+    or move; unique bytes of the workload's storage type)."""
     P, L, T, d, N, Hq, Hkv, B, m = w.P, w.L, w.T, w.head_dim, w.n_layers, w.n_q_heads, w.n_kv_heads, w.batch, w.m
-    e = 2
+    e = 2 if w.dtype == "bf16" else 4
     kv_bytes_per_pos = N * Hkv * d * e * 2          # K and V, all layers and KV heads
     rows = B * P
     q_bytes = N * rows * Hq * d * e
