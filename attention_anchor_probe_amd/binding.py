@@ -126,6 +126,17 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _scratch(nbytes, device, stream):
+    """A workspace for one call, allocated on the stream the call runs on: the
+    caching allocator then hands its memory out again only to work ordered
+    after the call's kernels on that stream."""
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream), device=device)
+    with torch.cuda.stream(s):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def make_pool(k, v, page_size=None):
     """KVPool over tensors k, v of shape [n_layers][n_pages][n_kv_heads][page_size][head_dim]."""
     if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 5:
@@ -167,7 +178,7 @@ def acache_probe_scores(pool_k, pool_v, q, masked_rows, masked_offsets, shared_s
         scale = 1.0 / math.sqrt(d)
     need = acache_probe_workspace_bytes(n_rows, B, L, hq, n_layers, lse_aff is not None)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(max(need, 1), q.device, stream)
     st = _lib().acache_probe_scores(
         ctypes.byref(pool), _dev(q, pool_k.dtype), n_rows, _dev(masked_rows, torch.int32),
         _dev(masked_offsets, torch.int32), masked_rows.numel(), int(max_masked), _dev(shared_slots, torch.int32), L, B,
@@ -207,7 +218,7 @@ def acache_probe_column_mass(pool_k, pool_v, q, masked_rows, masked_offsets, sha
         scale = 1.0 / math.sqrt(d)
     need = acache_probe_column_mass_workspace_bytes(B, L, hq, n_layers)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(max(need, 1), q.device, stream)
     st = _lib().acache_probe_column_mass(
         ctypes.byref(pool), _dev(q, pool_k.dtype), n_rows, _dev(masked_rows, torch.int32),
         _dev(masked_offsets, torch.int32), masked_rows.numel(), int(max_masked), _dev(shared_slots, torch.int32), L,
@@ -268,7 +279,7 @@ def acache_mapped_attention(pool_k, pool_v, q, q_offsets, read_slot, kv_offsets,
     _check("acache_mapped_attention_workspace_bytes",
            _lib().acache_mapped_attention_workspace_bytes(B, n_q, hq, n_layers, ctypes.byref(ws_bytes)))
     if workspace is None and ws_bytes.value > 0:
-        workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(ws_bytes.value, q.device, stream)
     st = _lib().acache_mapped_attention(
         ctypes.byref(pool), _dev(q, pool_k.dtype), _dev(q_offsets, torch.int32), n_q, int(max_q_per_req),
         _dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32), int(max_kv_per_req), B, hq, layer_begin,
@@ -305,7 +316,7 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
             pool_k, pool_v, B=B, n_q=n_q, max_q_per_req=max_q_per_req, n_q_heads=hq, n_layers=n_layers,
             max_kv_per_req=max_kv_per_req, L=L)
         if nb > 0:
-            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+            workspace = _scratch(nb, q.device, stream)
     st = _lib().acache_mapped_attention_shared(
         ctypes.byref(pool), _dev(q, pool_k.dtype), _dev(q_offsets, torch.int32), n_q, int(max_q_per_req),
         _dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32), int(max_kv_per_req),
@@ -342,7 +353,7 @@ def acache_store_attend(pool_k, pool_v, k_src, v_src, src_pos, src_slot, src_off
         nb = acache_store_attend_workspace_bytes(pool_k, pool_v, B=B, max_q_per_req=max_q_per_req,
                                                  max_kv_per_req=max_kv_per_req)
         if nb > 0:
-            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+            workspace = _scratch(nb, q.device, stream)
     st = _lib().acache_store_attend(
         ctypes.byref(pool), _dev(k_src, pool_k.dtype), _dev(v_src, pool_k.dtype), _dev(src_pos, torch.int32),
         _dev(src_slot, torch.int32), _dev(src_offsets, torch.int32), n_src, _dev(q, pool_k.dtype),

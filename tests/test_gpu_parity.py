@@ -564,6 +564,50 @@ def test_column_mass_ragged_masked_sets(dtype, d, hq, hkv):
     assert torch.equal(scores, before)
 
 
+def test_calls_on_other_streams():
+    """Every call takes the stream to run on (a torch stream or a raw
+    handle); workspaces the binding allocates itself live on that stream.
+    An admission and a decode step (probe, Top-K and maps, store-then-attend,
+    shared-affix read-slot attention) on a side stream equal the same calls
+    on the current stream, bit for bit."""
+    w = SMALL[1][1]
+    c = Chain(w, seed=5)
+    lay = c.lay
+    max_r = int(np.diff(lay.rc_offsets).max())
+    keep = [i32(x) for x in (lay.seq_len, lay.shared_slots, lay.private_pages, lay.private_page_offsets,
+                             lay.kv_offsets, lay.rc_offsets, lay.masked_rows, lay.masked_offsets)]
+    qr = gen.make_rows(w, c.n_rc, gen.S_QRC, device=DEV, heads=w.n_q_heads, seed=5)
+
+    def run(stream):
+        k, v = c.k.clone(), c.v.clone()
+        scores = torch.zeros((w.batch, w.L), device=DEV)
+        anchors = torch.empty((w.batch, c.K), dtype=torch.int32, device=DEV)
+        read = torch.empty(int(lay.kv_offsets[-1]), dtype=torch.int32, device=DEV)
+        rcp = torch.empty(c.n_rc, dtype=torch.int32, device=DEV)
+        rcs = torch.empty_like(rcp)
+        orc = torch.empty_like(qr)
+        out = torch.empty_like(c.qd)
+        maps = A.map_args(w.batch, w.affix_l, w.L, c.K, w.page_size, w.T, *keep[:6], read, rcp, rcs)
+        torch.cuda.synchronize()   # the copies and fills above are done before another stream reads them
+        A.acache_probe_scores(k, v, c.q, keep[6], keep[7], keep[1], scores, max_masked=w.m, stream=stream)
+        A.acache_topk_anchors(scores, c.K, w.affix_l, anchors, maps, stream=stream)
+        A.acache_store_attend(k, v, c.src_k, c.src_v, rcp, rcs, keep[5], qr, keep[5], read, keep[4], orc,
+                              max_q_per_req=max_r, max_kv_per_req=w.T, stream=stream)
+        A.acache_mapped_attention_shared(k, v, c.qd, i32(c.q_off), read, keep[4], keep[1], out, affix_l=w.affix_l,
+                                         max_q_per_req=c.n_dec, max_kv_per_req=w.T, stream=stream)
+        return scores, anchors, orc, out, k, v
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for stream in (side, side.cuda_stream):
+        got = run(stream)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("scores", "anchors", "store-then-attend O", "shared-affix O", "pool k", "pool v"),
+                              got, ref):
+            assert torch.equal(x, y), f"{name} on stream {stream!r}"
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_dropna_attention(idx):
     """DropNA (Section 5.3): the recompute map doubles as the read table with
