@@ -417,6 +417,14 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return (const char*)(((uint64_t)hi << 32) | lo);
 }
 
+// x on the lanes whose bit of `lanes` is clear, y on the others: one
+// v_cndmask with a scalar lane mask (the mask is built on the scalar unit)
+__device__ __forceinline__ float select_lanes(float x, float y, uint64_t lanes) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "s"(lanes));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -555,21 +563,36 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // of the iteration before the one that takes their softmax: the body of an
   // iteration (next scores, this tile's exponentials and P.V) is then free of
   // branches, so the matrix and vector work of one wave can interleave.
-  auto settle = [&](f32x16* s, int tile) {
+  // EXCL: the tile's two exclusion words (one per 32-key half) are loaded
+  // with vector loads two tiles ahead (a scalar load would have to wait for
+  // every LDS read in flight) and taken into scalar registers after the wait
+  // that opens the iteration
+  auto xload = [&](int tile, uint32_t* x) {
+    if constexpr (EXCL) {
+      if (tile < ntiles) {
+        x[0] = src.excl[2 * tile];
+        x[1] = src.excl[2 * tile + 1];
+      }
+    }
+  };
+  auto settle = [&](f32x16* s, int tile, uint32_t e0, uint32_t e1) {
     const int kb = tile * RB;
     if constexpr (EXCL) {
       // dropped keys (and the padding past the list) score -inf; lane half
       // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
-      const __attribute__((address_space(4))) uint32_t* exw =
-          (const __attribute__((address_space(4))) uint32_t*)src.excl;
-      const uint32_t e0 = exw[2 * tile], e1 = exw[2 * tile + 1];
       if ((e0 | e1) != 0u) {
+        // element i of lane half g2 is key 8*(i/4) + 4*g2 + i%4: its bit for
+        // lanes 0..31 and lanes 32..63 forms a 64-bit lane mask
+        const float ninf = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const uint32_t wl = (sub ? e1 : e0) >> (4 * g2);
+          const uint32_t w = sub ? e1 : e0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if ((wl >> (8 * (i >> 2) + (i & 3))) & 1u) s[sub][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t k = 8 * (i >> 2) + (i & 3);
+            const uint32_t lo = 0u - ((w >> k) & 1u), hi = 0u - ((w >> (k + 4)) & 1u);
+            s[sub][i] = select_lanes(s[sub][i], ninf, ((uint64_t)hi << 32) | lo);
+          }
         }
       }
     } else if (kb + RB > nk) {
@@ -629,9 +652,17 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   };
   // one iteration: sc holds the settled scores of tile t, sn receives those
   // of t+1; oc holds the row offsets of tile t+1, on receives those of t+2
-  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on) {
+  // xc holds the exclusion words of tile t+1, xn receives those of t+2
+  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on, const uint32_t* xc,
+                  uint32_t* xn) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
     wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
+    uint32_t f0 = 0, f1 = 0;
+    if constexpr (EXCL) {
+      f0 = __builtin_amdgcn_readfirstlane(xc[0]);
+      f1 = __builtin_amdgcn_readfirstlane(xc[1]);
+      xload(tile + 2, xn);
+    }
     if (tile + 2 < ntiles) {
       dma_k(tile + 2, on);
       if (tile + 3 < ntiles) sload(tile + 3);
@@ -642,15 +673,18 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     // computing them keeps the body branch-free
     scores(sn, tile + 1);
     absorb(sc, tile);
-    if (tile + 1 < ntiles) settle(sn, tile + 1);
+    if (tile + 1 < ntiles) settle(sn, tile + 1, f0, f1);
   };
 
   f32x16 sa[2], sb[2];
   uint32_t oa[4], ob[4];
+  uint32_t xa[2] = {0u, 0u}, xb[2] = {0u, 0u};
   if (ntiles > 0) {
     sload(0);
     dma_k(0, ob);
     dma_v(0, ob);
+    xload(0, xb);
+    xload(1, xa);
     if (ntiles > 1) {
       sload(1);
       dma_k(1, oa);
@@ -660,12 +694,12 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     wg_barrier();
     if (live) {
       scores(sa, 0);
-      settle(sa, 0);
+      settle(sa, 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
     }
   }
   for (int tile = 0; tile < ntiles; tile += 2) {
-    step(tile, sa, sb, oa, ob);
-    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa);
+    step(tile, sa, sb, oa, ob, xa, xb);
+    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa, xb, xa);
   }
 }
 
