@@ -25,6 +25,16 @@ design notes with their reasons):
     ascending logical positions.
   * Private slot i of a request is assigned in ascending logical order of
     the recompute set R = A u (non-affix positions).
+
+Pins.  Every function here is checked against something other than itself
+(hand-worked fixtures, closed forms, library routines on special cases, a
+pure-Python brute force; see the oracle tests).  Three readings of the paper
+stay parity unpinned against the paper itself, because it prints no value
+that decides them: the affix-only normaliser of Eq. (4) (probe_layer; the
+full-context alternative is probe_layer_full), ceil rather than round in
+anchor_count (they differ at L = 4096 and 16384), and the squared-L2 reduction
+of the KV difference in hkvd_scores.  Each function is pinned to the
+mathematics of its reading.
 """
 import math
 import numpy as np
