@@ -87,6 +87,11 @@ SMALL = [
                                 page_order="random")),
     ("bf16-d16-ps4", Workload(95, "s5", "bf16", 1, 2, 1, 16, (("affix", 45), ("req", 3), ("gen", 19)), 2, 0.2,
                               page_size=4, page_order="random")),
+    # large pages: a page holds many slots of every KV head
+    ("bf16-d128-ps64", Workload(96, "s6", "bf16", 2, 4, 4, 128, (("affix", 333), ("req", 20), ("gen", 48)), 3, 0.2,
+                                page_size=64, page_order="random")),
+    ("bf16-d128-ps256-gqa", Workload(97, "s7", "bf16", 1, 8, 2, 128, (("req", 11), ("affix", 600), ("gen", 70)), 2,
+                                     0.25, page_size=256, page_order="fragmented", free_frac=0.125)),
 ]
 
 
