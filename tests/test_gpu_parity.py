@@ -613,6 +613,53 @@ def test_calls_on_other_streams():
             assert torch.equal(x, y), f"{name} on stream {stream!r}"
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.7])
+def test_softmax_scale_is_honoured(scale):
+    """Every call takes the softmax scale (Eq. 4 divides by sqrt(d) by
+    default); a scale far below and far above it gives the oracle's probe
+    scores, O_aff and LSE, and the oracle's read-slot attention through both
+    read-slot calls."""
+    w = SMALL[1][1]
+    c = Chain(w, seed=6)
+    lay, h = c.lay, c.h
+    scores = torch.zeros((w.batch, w.L), device=DEV)
+    o_aff = torch.empty_like(c.q)
+    lse_aff = torch.empty(c.q.shape[:3], device=DEV)
+    A.acache_probe_scores(c.k, c.v, c.q, i32(lay.masked_rows), i32(lay.masked_offsets), i32(lay.shared_slots),
+                          scores, max_masked=w.m, o_aff=o_aff, lse_aff=lse_aff, scale=scale)
+    read = np.concatenate([O.build_maps(np.arange(c.K) + w.affix_l, int(lay.seq_len[b]), w.affix_l, w.L,
+                                        lay.shared_slots,
+                                        lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]],
+                                        w.page_size)[0] for b in range(w.batch)])
+    out = torch.empty_like(c.qd)
+    lse = torch.empty(c.qd.shape[:3], device=DEV)
+    out_sh = torch.empty_like(c.qd)
+    lse_sh = torch.empty(c.qd.shape[:3], device=DEV)
+    A.acache_mapped_attention(c.k, c.v, c.qd, i32(c.q_off), i32(read), i32(lay.kv_offsets), out, lse=lse,
+                              max_q_per_req=c.n_dec, max_kv_per_req=w.T, scale=scale)
+    A.acache_mapped_attention_shared(c.k, c.v, c.qd, i32(c.q_off), i32(read), i32(lay.kv_offsets),
+                                     i32(lay.shared_slots), out_sh, lse=lse_sh, affix_l=w.affix_l,
+                                     max_q_per_req=c.n_dec, max_kv_per_req=w.T, scale=scale)
+    torch.cuda.synchronize()
+    s_ref = np.zeros((w.batch, w.L))
+    for n in range(w.n_layers):
+        o_r, l_r, s_n = O.probe_layer(h["q"][n], h["k"][n], h["v"][n], lay.shared_slots, w.page_size, w.n_kv_heads,
+                                      lay.masked_rows, lay.masked_offsets, scale)
+        s_ref += s_n
+        ok, st = bf16_close(o_aff[n].float().cpu().numpy(), o_r)
+        assert ok, f"O_aff layer {n}: {st}"
+        np.testing.assert_allclose(lse_aff[n].cpu().numpy(), l_r, atol=1e-4)
+        o_m, l_m = O.mapped_attention_layer(h["qd"][n], h["k"][n], h["v"][n], c.q_off, read, lay.kv_offsets,
+                                            w.n_kv_heads, w.page_size, scale)
+        for name, got_o, got_l in (("single pass", out, lse), ("shared affix", out_sh, lse_sh)):
+            ok, st = bf16_close(got_o[n].float().cpu().numpy(), o_m)
+            assert ok, f"{name} O layer {n}: {st}"
+            np.testing.assert_allclose(got_l[n].cpu().numpy(), l_m, atol=1e-4)
+    s_gpu = scores.cpu().numpy().astype(np.float64)
+    big = s_ref >= 1e-6 * s_ref.max()
+    assert (np.abs(s_gpu - s_ref)[big] / s_ref[big]).max() <= 1e-3
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_dropna_attention(idx):
     """DropNA (Section 5.3): the recompute map doubles as the read table with
