@@ -660,6 +660,33 @@ def test_softmax_scale_is_honoured(scale):
     assert (np.abs(s_gpu - s_ref)[big] / s_ref[big]).max() <= 1e-3
 
 
+def test_layer_subset_calls_match_whole_calls():
+    """A call over layers layer_begin .. layer_begin+n-1 (q holding only those
+    layers) computes what the whole-stack call computes for them, bit for
+    bit: the probe, both read-slot calls and the column mass."""
+    w = SMALL[2][1]
+    c = Chain(w, seed=8)
+    c.run_gpu()
+    lay = c.lay
+    for n in range(w.n_layers):
+        q1, qd1 = c.q[n:n + 1].contiguous(), c.qd[n:n + 1].contiguous()
+        o_aff = torch.empty_like(q1)
+        lse_aff = torch.empty(q1.shape[:3], device=DEV)
+        A.acache_probe_attention(c.k, c.v, q1, i32(lay.shared_slots), lse_aff, o_aff=o_aff, layer_begin=n)
+        out = torch.empty_like(qd1)
+        out_sh = torch.empty_like(qd1)
+        A.acache_mapped_attention(c.k, c.v, qd1, i32(c.q_off), c.read_slot, i32(lay.kv_offsets), out,
+                                  max_q_per_req=c.n_dec, max_kv_per_req=w.T, layer_begin=n)
+        A.acache_mapped_attention_shared(c.k, c.v, qd1, i32(c.q_off), c.read_slot, i32(lay.kv_offsets),
+                                         i32(lay.shared_slots), out_sh, affix_l=w.affix_l, max_q_per_req=c.n_dec,
+                                         max_kv_per_req=w.T, layer_begin=n)
+        torch.cuda.synchronize()
+        assert torch.equal(o_aff[0], c.o_aff[n]), f"probe O_aff, layer {n}"
+        assert torch.equal(lse_aff[0], c.lse_aff[n]), f"probe LSE, layer {n}"
+        assert torch.equal(out[0], c.out[n]), f"single-pass read-slot attention, layer {n}"
+        assert torch.equal(out_sh[0], c.out_sh[n]), f"shared-affix read-slot attention, layer {n}"
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_dropna_attention(idx):
     """DropNA (Section 5.3): the recompute map doubles as the read table with
