@@ -2,9 +2,10 @@
 
 Argument marshalling only: each function checks tensor placement, dtype and
 contiguity, turns tensors into device pointers and calls the C entry point of
-the same name on torch's current HIP stream.  Every step of the path runs in
-the library's HIP kernels; nothing here computes.  If the library is missing
-the import fails: there is no fallback.
+the same name on the given stream (torch's current HIP stream by default);
+workspaces it allocates itself are allocated on that stream.  Every step of
+the path runs in the library's HIP kernels; nothing here computes.  If the
+library is missing the first call fails: there is no fallback.
 """
 import ctypes
 import math
