@@ -323,7 +323,8 @@ def test_shared_affix_attention_seeded(case, hkv):
         np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
 
 
-@pytest.mark.parametrize("hq,hkv", [(28, 4), (8, 2), (8, 4)], ids=["g7-packed", "g4-packed", "g2-unpacked"])
+@pytest.mark.parametrize("hq,hkv", [(28, 4), (8, 2), (8, 4), (32, 2), (16, 1)],
+                         ids=["g7-packed", "g4-packed", "g2-unpacked", "g16-packed", "g16-mqa-packed"])
 def test_gqa_decode_attention_packed(hq, hkv):
     """Decode blocks of grouped-query heads: with hq/hkv query heads per KV
     head and 32-row blocks, groups of 7 and 4 fill a 128-row tile and run
