@@ -92,6 +92,9 @@ SMALL = [
                                 page_size=64, page_order="random")),
     ("bf16-d128-ps256-gqa", Workload(97, "s7", "bf16", 1, 8, 2, 128, (("req", 11), ("affix", 600), ("gen", 70)), 2,
                                      0.25, page_size=256, page_order="fragmented", free_frac=0.125)),
+    # sixteen query heads per KV head: the probe's packed units hold 16 heads' rows
+    ("bf16-d128-g16", Workload(98, "s8", "bf16", 1, 32, 2, 128, (("affix", 200), ("req", 12), ("gen", 40)), 2, 0.2,
+                               page_order="random")),
 ]
 
 
