@@ -55,7 +55,8 @@ _SIG = {
                              _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "acache_probe_attention": ([ctypes.POINTER(KVPool), _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P],
                                ctypes.c_int),
-    "acache_probe_column_mass_workspace_bytes": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_probe_column_mass_workspace_bytes": ([_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+                                                 ctypes.c_int),
     "acache_probe_column_mass": ([ctypes.POINTER(KVPool), _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I,
                                   ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "acache_topk_anchors": ([_P, _I, _I, _I, _I, _P, ctypes.POINTER(MapArgs), _P], ctypes.c_int),
@@ -202,10 +203,10 @@ def acache_probe_attention(pool_k, pool_v, q, shared_slots, lse_aff, *, o_aff=No
     _check("acache_probe_attention", st)
 
 
-def acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers):
+def acache_probe_column_mass_workspace_bytes(n_rows, B, L, n_q_heads, n_layers):
     out = ctypes.c_size_t()
     _check("acache_probe_column_mass_workspace_bytes",
-           _lib().acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, ctypes.byref(out)))
+           _lib().acache_probe_column_mass_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, ctypes.byref(out)))
     return out.value
 
 
@@ -217,7 +218,7 @@ def acache_probe_column_mass(pool_k, pool_v, q, masked_rows, masked_offsets, sha
     B, L = scores.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = acache_probe_column_mass_workspace_bytes(B, L, hq, n_layers)
+    need = acache_probe_column_mass_workspace_bytes(n_rows, B, L, hq, n_layers)
     if workspace is None:
         workspace = _scratch(max(need, 1), q.device, stream)
     st = _lib().acache_probe_column_mass(

@@ -104,12 +104,15 @@ int acache_anchor_count(int32_t L, double rate, int32_t* K_out) {
   return ACACHE_OK;
 }
 
-int acache_probe_column_mass_workspace_bytes(int32_t B, int32_t L, int32_t n_q_heads, int32_t n_layers,
-                                             size_t* bytes) {
-  if (!bytes || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
+int acache_probe_column_mass_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n_q_heads,
+                                             int32_t n_layers, size_t* bytes) {
+  if (!bytes || n_rows < 0 || B < 0 || L < 0 || n_q_heads < 0 || n_layers < 0) return ACACHE_EINVAL;
   // partial column masses: one per (layer, query head, request, key) on the
-  // MFMA path, one per (layer, request, key) on the vector path
-  *bytes = align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float));
+  // MFMA path, one per (layer, request, key) on the vector path; then the
+  // masked rows' scaled LSE per (layer, query head), every request padded to
+  // whole 32-row tiles (at most n_rows + 31 * B values)
+  *bytes = align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float)) +
+           align_up((size_t)n_layers * n_q_heads * ((size_t)n_rows + 31 * (size_t)B) * sizeof(float));
   return ACACHE_OK;
 }
 
@@ -119,7 +122,7 @@ int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n
   size_t ws = 0;
   if (!lse_given) ws += align_up((size_t)n_layers * n_rows * n_q_heads * sizeof(float));
   size_t cm = 0;
-  acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, &cm);
+  acache_probe_column_mass_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, &cm);
   *bytes = ws + cm;
   return ACACHE_OK;
 }
@@ -192,6 +195,8 @@ hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, i
   c.scale = scale;
   c.lse = lse;
   c.partial = partial;
+  c.lse_stride = (size_t)n_rows + 31 * (size_t)B;
+  c.lse_prep = partial + align_up((size_t)n_layers * n_q_heads * B * L * sizeof(float)) / sizeof(float);
   const bool mf = mfma_supported(pool->dtype, pool->head_dim);
   if (dry) return mf ? launch_colmass_mfma(c, s, true) : hipSuccess;
   hipError_t e = mf ? launch_colmass_mfma(c, s) : launch_colmass_generic(c, pool->dtype, s);
@@ -225,13 +230,13 @@ int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t 
   int st;
   if ((st = check_probe_common(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale)))
     return st;
-  if (B < 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (B < 0 || n_masked < 0 || n_masked > n_rows || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
   if (B > 65535) return ACACHE_ESHAPE;
   if (!scores || !lse_aff) return ACACHE_EINVAL;
   if (n_masked > 0 && !masked_rows) return ACACHE_EINVAL;
   if (B > 0 && !masked_offsets) return ACACHE_EINVAL;
   size_t need = 0;
-  acache_probe_column_mass_workspace_bytes(B, L, n_q_heads, n_layers, &need);
+  acache_probe_column_mass_workspace_bytes(n_rows, B, L, n_q_heads, n_layers, &need);
   if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
     return ACACHE_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -252,7 +257,7 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
   int st;
   if ((st = check_probe_common(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale)))
     return st;
-  if (B < 0 || n_masked < 0 || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
+  if (B < 0 || n_masked < 0 || n_masked > n_rows || max_masked < 0 || max_masked > n_masked) return ACACHE_EINVAL;
   if (B > 65535) return ACACHE_ESHAPE;
   if (!scores) return ACACHE_EINVAL;
   if (n_masked > 0 && !masked_rows) return ACACHE_EINVAL;

@@ -81,6 +81,12 @@ struct ColmassArgs {
   float scale;
   const float* lse;
   float* partial;
+  // MFMA path: each masked row's LSE scaled to -LSE/scale, per (layer, query
+  // head), every request's rows padded with -inf to whole 32-row tiles
+  // (request b's rows start at masked_offsets[b] + 31 * b); lse_stride floats
+  // per (layer, query head)
+  float* lse_prep;
+  size_t lse_stride;
 };
 
 hipError_t launch_topk(const float* scores, int B, int L, int K, int affix_l, int32_t* anchors, hipStream_t st);

@@ -109,6 +109,8 @@ struct ColP {
   float c2;
   const float* lse;
   float* partial;  // [n_layers][n_q_heads][B][L]
+  const float* lse_prep;  // per (layer, query head): -LSE/scale of the masked rows, padded
+  size_t lse_stride;
   int key_blocks;
   int n_units;
   int per_xcd;
@@ -406,6 +408,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
+}
+
+// One 4-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
+// address lds_base + 4 * i (same waiting rules as dma16).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
 }
 
 // A wave-uniform pointer, asserted to the compiler so that it stays in scalar
@@ -1089,7 +1097,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
 // the iteration.  The loop is software pipelined: while a wave takes the
 // exponentials of tile t, it computes the scores of tile t+1.  Each score
 // accumulator starts at -LSE/scale of its row, so that the weight is
-// exp2(c2 * accumulator).
+// exp2(c2 * accumulator); those values come prepared by colmass_lse_prep
+// (padded with -inf to whole tiles) and reach LDS by direct loads too.
 __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   __shared__ __attribute__((aligned(1024))) char Qs[2][32 * ROWB];
   __shared__ __attribute__((aligned(16))) float lse2[2][32];
@@ -1152,15 +1161,12 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   const char* qhead = (const char*)(p.q + ((size_t)n * p.n_rows * p.n_q_heads + h) * D);
   const size_t qrow_bytes = (size_t)p.n_q_heads * D * sizeof(bf16_t);
   const uint32_t lds_q = lds_addr(&Qs[0][0]) + 8 * wave * ROWB;
-  const float neg_inv_scale = -kLog2e / p.c2;
-  // masked-row indices of a tile: the two rows this lane moves, and row
-  // lane%32 (whose LSE lanes 0..31 stage)
-  struct RowIdx { int ra, rb, rl; };
+  // masked-row indices of a tile: the two rows this lane moves
+  struct RowIdx { int ra, rb; };
   auto rows_load = [&](It t) -> RowIdx {
     RowIdx ix;
     ix.ra = p.masked_rows[min(t.r0 + ra, t.m1 - 1)];
     ix.rb = p.masked_rows[min(t.r0 + ra + 4, t.m1 - 1)];
-    ix.rl = p.masked_rows[min(t.r0 + l32, t.m1 - 1)];
     return ix;
   };
   auto dma_q = [&](int stage, const RowIdx& ix) {
@@ -1168,12 +1174,12 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     dma16(qhead + (size_t)ix.ra * qrow_bytes + gchunk0, dst);
     dma16(qhead + (size_t)ix.rb * qrow_bytes + gchunk1, dst + 4 * ROWB);
   };
-  // every lane loads the LSE of row lane%32; lanes 0..31 store it, an
-  // iteration later (rows past the request's end start at -inf, so they add
-  // exp2(-inf) = 0)
-  auto lse_load = [&](const RowIdx& ix) { return p.lse[((size_t)n * p.n_rows + ix.rl) * p.n_q_heads + h]; };
-  auto lse_store = [&](int stage, It t, float l) {
-    if (tid < 32) lse2[stage][tid] = t.r0 + tid < t.m1 ? l * neg_inv_scale : -INFINITY;
+  // the tile's 32 prepared accumulator starts (-inf past the request's
+  // rows, so they add exp2(-inf) = 0), moved by lanes 0..31 of wave 0
+  const float* lprep = p.lse_prep + (size_t)(n * p.n_q_heads + h) * p.lse_stride;
+  auto dma_lse = [&](int stage, It t) {
+    if (wave == 0 && lane < 32)
+      dma4(lprep + t.r0 + 31 * (size_t)t.b + lane, __builtin_amdgcn_readfirstlane(lds_addr(&lse2[stage][0])));
   };
   // scores of the tile in stage st, from accumulators that start at its
   // rows' -LSE/scale
@@ -1195,17 +1201,15 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     }
   };
 
-  // prologue: tiles t0 and t1 loading into stages 0 and 1, t1's LSE in
-  // registers, t2's row indices
+  // prologue: tiles t0 and t1 loading into stages 0 and 1, t2's row indices
   It t1 = next(t0), t2 = next(t1), t3 = next(t2);
-  {
-    const RowIdx i0 = rows_load(t0);
-    dma_q(0, i0);
-    lse_store(0, t0, lse_load(i0));
-  }
+  dma_q(0, rows_load(t0));
+  dma_lse(0, t0);
   RowIdx in = rows_load(t1);
-  dma_q(1, in);
-  float lq = lse_load(in);
+  if (t1.b < p.B) {
+    dma_q(1, in);
+    dma_lse(1, t1);
+  }
   in = rows_load(t2);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tile t0 (and t1) in LDS, t2's indices in registers
   __syncthreads();
@@ -1217,12 +1221,11 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   // one tile: sc holds the scores of t0, sn receives those of t1
   auto step = [&](f32x16* sc, f32x16* sn) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's loads of t1 (and t2's indices) landed
-    lse_store(st ^ 1, t1, lq);
     __syncthreads();  // t1 is in stage st^1 for every wave; no wave still reads stage st
     // tile t2 into stage st, and the indices of t3, while this iteration computes
     if (t2.b < p.B) {
       dma_q(st, in);
-      lq = lse_load(in);
+      dma_lse(st, t2);
     }
     const It t4 = next(t3);
     in = rows_load(t3);
@@ -1255,6 +1258,25 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     step(sb, sa);
     if (t0.b >= p.B) break;
   }
+}
+
+// The column mass's accumulator starts: for every (layer, query head) and
+// request b, -LSE/scale of the request's masked rows in order, then -inf up to
+// a whole number of 32-row tiles, starting at masked_offsets[b] + 31 * b.
+__global__ __launch_bounds__(256) void colmass_lse_prep(const float* __restrict__ lse,
+                                                        const int32_t* __restrict__ masked_rows,
+                                                        const int32_t* __restrict__ masked_offsets, int n_rows,
+                                                        int n_q_heads, int x_tiles, float neg_inv_scale,
+                                                        float* __restrict__ out, size_t stride) {
+  const int nh = blockIdx.x / x_tiles;  // layer * n_q_heads + query head
+  const int i = (blockIdx.x - nh * x_tiles) * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  const int n = nh / n_q_heads, h = nh - n * n_q_heads;
+  const int m0 = masked_offsets[b], m = masked_offsets[b + 1] - m0;
+  if (i >= ((m + 31) & ~31)) return;
+  float v = -INFINITY;
+  if (i < m) v = lse[((size_t)n * n_rows + masked_rows[m0 + i]) * n_q_heads + h] * neg_inv_scale;
+  out[(size_t)nh * stride + m0 + 31 * (size_t)b + i] = v;
 }
 
 bool mfma_supported(int dtype, int head_dim) { return dtype == ACACHE_BF16 && head_dim == D; }
@@ -1396,13 +1418,22 @@ hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_ru
   p.c2 = a.scale * kLog2e;
   p.lse = a.lse;
   p.partial = a.partial;
+  p.lse_prep = a.lse_prep;
+  p.lse_stride = a.lse_stride;
   p.key_blocks = (a.L + 255) / 256;
   const long long units = (long long)a.n_layers * a.n_q_heads * p.key_blocks;
   if (units == 0) return hipSuccess;
   if (units > (1ll << 30)) return hipErrorInvalidValue;
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
+  const int x_tiles = (((a.max_masked + 31) & ~31) + 255) / 256;
+  if ((long long)x_tiles * a.n_layers * a.n_q_heads > (1ll << 31) - 1 || a.B > 65535) return hipErrorInvalidValue;
   if (dry_run) return hipSuccess;
+  if (x_tiles > 0 && a.B > 0) {
+    hipLaunchKernelGGL(colmass_lse_prep, dim3(x_tiles * a.n_layers * a.n_q_heads, a.B), dim3(256), 0, st, a.lse,
+                       a.masked_rows, a.masked_offsets, a.n_rows, a.n_q_heads, x_tiles, -1.0f / a.scale,
+                       a.lse_prep, a.lse_stride);
+  }
   hipLaunchKernelGGL(colmass_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }

@@ -86,7 +86,7 @@ class Setup:
         self.o_aff = torch.empty_like(self.q)
         self.lse_aff = torch.empty(self.q.shape[:3], device=dev)
         self.scores = torch.zeros((w.batch, w.L), device=dev)
-        ws = A.acache_probe_column_mass_workspace_bytes(w.batch, w.L, w.n_q_heads, w.n_layers)
+        ws = A.acache_probe_column_mass_workspace_bytes(self.q.shape[1], w.batch, w.L, w.n_q_heads, w.n_layers)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.anchors = torch.empty((w.batch, self.K), dtype=torch.int32, device=dev)
         self.read_slot = torch.empty(int(lay.kv_offsets[-1]), dtype=torch.int32, device=dev)
@@ -304,7 +304,7 @@ class Setup:
         lse1 = torch.empty(q1.shape[:3], device=self.dev)
         mrows, moff = i32(lay.masked_rows[m0:m1] - r0), i32([0, m1 - m0])
         sc = torch.zeros((1, w.L), device=self.dev)
-        ws = torch.empty(A.acache_probe_column_mass_workspace_bytes(1, w.L, w.n_q_heads, w.n_layers),
+        ws = torch.empty(A.acache_probe_column_mass_workspace_bytes(q1.shape[1], 1, w.L, w.n_q_heads, w.n_layers),
                          dtype=torch.uint8, device=self.dev)
         an = torch.empty((1, self.K), dtype=torch.int32, device=self.dev)
 

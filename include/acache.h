@@ -110,8 +110,9 @@ int acache_anchor_count(int32_t L, double rate, int32_t* K_out);
  *  masked_rows     [n_masked] row indices into q of the initially masked rows,
  *                  request b's at masked_offsets[b] .. masked_offsets[b+1]-1
  *  masked_offsets  [B+1]
- *  n_masked        masked_offsets[B] (host copy, sizes the launch)
- *  max_masked      max over b of masked_offsets[b+1]-masked_offsets[b] (host)
+ *  n_masked        masked_offsets[B] (host copy, sizes the launch); at most n_rows
+ *  max_masked      max over b of masked_offsets[b+1]-masked_offsets[b] (host;
+ *                  a smaller value gives wrong scores for the longer requests)
  *  shared_slots    [L] physical slot of affix offset j
  *  scale           softmax scale, normally 1/sqrt(head_dim) (Eq. 4)
  *  scores          [B][L] fp32, ACCUMULATED (+=), so per-layer-group calls sum
@@ -151,7 +152,7 @@ int acache_probe_attention(const acache_kv_pool* pool, const void* q, int32_t n_
                            int32_t layer_begin, int32_t n_layers, float scale, void* o_aff,
                            float* lse_aff, acache_stream_t stream);
 
-int acache_probe_column_mass_workspace_bytes(int32_t B, int32_t L, int32_t n_q_heads,
+int acache_probe_column_mass_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n_q_heads,
                                              int32_t n_layers, size_t* bytes /*host*/);
 
 int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t n_rows,
