@@ -1191,13 +1191,18 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     f32x16 init;
 #pragma unroll
     for (int i = 0; i < 16; ++i) init[i] = lse2[st][8 * (i >> 2) + 4 * g2 + (i & 3)];
+    // all eight Q fragments read before the first product, so the LDS
+    // reads overlap one another instead of each waiting for its MFMA pair
+    bf16x8 qv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[c] = as_bf16x8(*(const u32x4*)(qs + qrd[c]));
+    __builtin_amdgcn_sched_barrier(0);
     s[0] = init;
     s[1] = init;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const bf16x8 qa = as_bf16x8(*(const u32x4*)(qs + qrd[c]));
-      s[0] = mfma(qa, kf[0][c], s[0]);
-      s[1] = mfma(qa, kf[1][c], s[1]);
+      s[0] = mfma(qv[c], kf[0][c], s[0]);
+      s[1] = mfma(qv[c], kf[1][c], s[1]);
     }
   };
 
