@@ -559,12 +559,17 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     s[0] = f32x16{};
     s[1] = f32x16{};
     // the two 32-key halves alternate, so that two independent accumulation
-    // chains share the matrix pipe
+    // chains share the matrix pipe.  In the shared-affix decode (EXCL), where
+    // workgroups in the memory-bound private phase share the CU, the score
+    // block runs at raised wave priority; in the many-query kernels, where
+    // every wave is matrix-bound, raising it was slower
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(0);
   };
   // Scores of a tile are masked, and the running max updated (with the lazy
   // rescale of O and the row sum), as soon as they are computed, at the end
