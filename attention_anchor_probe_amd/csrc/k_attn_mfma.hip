@@ -560,16 +560,17 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     s[1] = f32x16{};
     // the two 32-key halves alternate, so that two independent accumulation
     // chains share the matrix pipe.  In the shared-affix decode (EXCL), where
-    // workgroups in the memory-bound private phase share the CU, the score
-    // block runs at raised wave priority; in the many-query kernels, where
-    // every wave is matrix-bound, raising it was slower
-    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
+    // workgroups in the memory-bound private phase share the CU, the shared
+    // phase runs at wave priority 1 and its score block at 2; in the
+    // many-query kernels, where every wave is matrix-bound, raising the
+    // priority was slower
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
-    if constexpr (EXCL) __builtin_amdgcn_s_setprio(0);
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
   };
   // Scores of a tile are masked, and the running max updated (with the lazy
   // rescale of O and the row sum), as soon as they are computed, at the end
@@ -1013,7 +1014,9 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     src.table = p.kv_table;
     src.nk = p.n_kv;
     src.excl = p.excl + (size_t)min(b, p.B - 1) * p.excl_words;
+    __builtin_amdgcn_s_setprio(1);  // ahead of the private phase's waves on the CU
     tile_loop<true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- private phase: this wave's own 32-key tiles, no workgroup barriers
