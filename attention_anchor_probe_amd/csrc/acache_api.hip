@@ -127,6 +127,8 @@ int acache_probe_workspace_bytes(int32_t n_rows, int32_t B, int32_t L, int32_t n
   return ACACHE_OK;
 }
 
+}  // extern "C"
+
 namespace {
 
 int check_probe_common(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* shared_slots,
@@ -205,6 +207,8 @@ hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, i
 }
 
 }  // namespace
+
+extern "C" {
 
 int acache_probe_attention(const acache_kv_pool* pool, const void* q, int32_t n_rows, const int32_t* shared_slots,
                            int32_t L, int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
@@ -345,6 +349,8 @@ int acache_mapped_attention_workspace_bytes(int32_t B, int32_t n_q, int32_t n_q_
   return ACACHE_OK;
 }
 
+}  // extern "C"
+
 namespace {
 // acache_mapped_attention: every check, then (dry == false) the launch
 int mapped_attention_impl(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
@@ -387,6 +393,8 @@ int mapped_attention_impl(const acache_kv_pool* pool, const void* q, const int32
 }
 }  // namespace
 
+extern "C" {
+
 int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets, int32_t n_q,
                             int32_t max_q_per_req, const int32_t* read_slot, const int32_t* kv_offsets,
                             int32_t max_kv_per_req, int32_t B, int32_t n_q_heads, int32_t layer_begin,
@@ -397,6 +405,8 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
   return mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
                                n_q_heads, layer_begin, n_layers, scale, out, lse, (hipStream_t)stream, false);
 }
+
+}  // extern "C"
 
 namespace {
 // workspace of the two-pass shared-affix attention (256-byte aligned parts)
@@ -429,6 +439,8 @@ SharedWs shared_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t n_q, in
   return w;
 }
 }  // namespace
+
+extern "C" {
 
 int acache_mapped_attention_shared_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t n_q,
                                                    int32_t max_q_per_req, int32_t n_q_heads, int32_t n_layers,
@@ -501,6 +513,8 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
   return status_of(launch_attn_mfma_shared(a, s));
 }
 
+}  // extern "C"
+
 namespace {
 // workspace of the fused store-then-attend path (256-byte aligned parts)
 struct StoreWs {
@@ -521,6 +535,8 @@ StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, in
   return w;
 }
 }  // namespace
+
+extern "C" {
 
 int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t max_q_per_req,
                                         int32_t max_kv_per_req, size_t* bytes) {

@@ -14,8 +14,9 @@ namespace acache {
 // Eight consecutive elements of one (row, head) per thread; the threads of a
 // pair are consecutive lanes of one wave (head_dim / 8 divides 64), so an
 // in-place LSE write by the pair's first lane follows every lane's read.
+// o may be oa (and l may be la): those two carry no restrict qualifier.
 template <typename T>
-__global__ __launch_bounds__(256) void lse_merge_kernel(const T* __restrict__ oa, const float* la,
+__global__ __launch_bounds__(256) void lse_merge_kernel(const T* oa, const float* la,
                                                         const T* __restrict__ ob, const float* __restrict__ lb,
                                                         T* o, float* l, long long n_pairs, int head_dim) {
   const int per = head_dim / 8;

@@ -43,6 +43,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden default visibility; the declarations of
+ * this header are its only exported symbols. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 typedef void* acache_stream_t; /* hipStream_t */
 
 enum acache_status {
@@ -411,6 +417,10 @@ int acache_kv_footprint(int32_t B, const int32_t* seq_len /*host*/, int32_t L, i
 int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner,
                           const int32_t* page_owner, int32_t n_pages, int32_t page_size,
                           int32_t distinct, int32_t* bad_index);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

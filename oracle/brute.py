@@ -127,3 +127,27 @@ def mapped_attention(q, k_pool, v_pool, q_offsets, read_slot, kv_offsets, n_kv, 
                     _, o, _ = _attend([_val(e) for e in q[n][r][h]], keys, vals, scale)
                     O[n][r][h] = o
     return O
+
+
+def block_slots(anchors, affix_l, L, private_pages, ps, block_start, block_len):
+    """Destination slots of each request's decode block, from the closed-form
+    private index of maps() (no read-slot table): request b's positions
+    block_start[b] .. +block_len, in request order.  anchors[b] and
+    private_pages[b] are request b's own lists.  Decode blocks lie outside
+    the affix or on anchors (private positions); a non-anchor affix position
+    is refused."""
+    out = []
+    for b in range(len(block_start)):
+        K = len(anchors[b])
+        rank = {a: r for r, a in enumerate(sorted(anchors[b]))}
+        for p in range(block_start[b], block_start[b] + block_len):
+            if p < affix_l:
+                i = p
+            elif p < affix_l + L:
+                if p not in rank:
+                    raise ValueError("a decode block inside the affix reads the shared region")
+                i = affix_l + rank[p]
+            else:
+                i = p - L + K
+            out.append(int(private_pages[b][i // ps]) * ps + i % ps)
+    return out

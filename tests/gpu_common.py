@@ -1,8 +1,12 @@
 """Helpers of the GPU parity tests: run the library's chain and the oracle's
 own chain on the same seeded inputs and compare stage by stage.
 
-The oracle only ever receives generator inputs (copied to the host before
-the library touches them); no library output is fed to it.
+The oracle receives generator inputs (copied to the host before the library
+touches them).  One library output is fed back, in compositional checks
+only: where the library's anchor set differs from the oracle's inside the
+tie band (after both have been compared against the oracle's scores), the
+oracle's maps, scatter and attention are recomputed from the library's
+anchors, so that those stages are still checked on that seed.
 """
 import math
 
@@ -125,11 +129,20 @@ class Chain:
             if n in layers:
                 self.r_oaff[n], self.r_lseaff[n] = o, lse
         self.r_anchors = [O.topk_anchors(self.r_scores[b], K, w.affix_l) for b in range(w.batch)]
+        self.run_oracle_downstream(self.r_anchors, layers)
+
+    def run_oracle_downstream(self, anchors, layers=None):
+        """The oracle's maps, scatter and read-slot attention from the anchor
+        sets `anchors` (the oracle's own, or the library's once they have been
+        checked against the oracle's scores up to the tie band)."""
+        w, lay, h = self.w, self.lay, self.h
+        layers = list(range(w.n_layers)) if layers is None else layers
+        self.r_anchors_used = [np.asarray(a) for a in anchors]
         rd, rp, rs = [], [], []
         for b in range(w.batch):
             pp = lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
-            r_, p_, s_ = O.build_maps(self.r_anchors[b], int(lay.seq_len[b]), w.affix_l, w.L, lay.shared_slots, pp,
-                                      w.page_size)
+            r_, p_, s_ = O.build_maps(self.r_anchors_used[b], int(lay.seq_len[b]), w.affix_l, w.L,
+                                      lay.shared_slots, pp, w.page_size)
             rd.append(r_); rp.append(p_); rs.append(s_)
         self.r_read, self.r_rcpos, self.r_rcslot = map(np.concatenate, (rd, rp, rs))
         kp, vp = h["k"][layers].copy(), h["v"][layers].copy()

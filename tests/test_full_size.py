@@ -13,10 +13,9 @@ Part A -- probe (Eq. 4-5) and Top-K (Eq. 6) on the seeded inputs
     layer alone) against the oracle for sampled requests;
   * O_aff and LSE_aff of sampled rows of sampled layers against the oracle;
   * the anchor set of one sampled request against the oracle's Top-K of its
-    own full-layer scores (exact beyond the 1e-3 tie band).  Not run at
-    L=16384 (the oracle would need ~10^12 fp64 operations); there the per-layer
-    scores, the total-mass invariant and the seeded Top-K at the same L and K
-    stand in.
+    own full-layer scores (exact beyond the 1e-3 tie band), on every workload;
+    at L=16384 that is ~10^12 fp64 operations, about a minute and a half of
+    host time, over a host copy of the shared pages (4.3 GB of affix keys).
 Part B -- maps, scatter, decode blocks and read-slot attention
   * anchors from a seeded Top-K (the same seeded scores on both sides; the
     library's Top-K must equal the oracle's bit for bit);
@@ -74,18 +73,16 @@ def test_full_size(cid):
     lay = gen.make_layout(w, K, seed=0)
     k, v = gen.make_pool(w, lay, device=DEV)
     q = gen.make_probe_q(w, lay, device=DEV)
-    layers = _sampled(w.n_layers, 1 if cid == 5 else 2, 100 + cid)
+    layers = _sampled(w.n_layers, 2, 100 + cid)
     reqs = _sampled(w.batch, 4, 200 + cid)
     # host snapshots of inputs, taken before the library runs
     hk = {n: np_of(k[n]) for n in layers}
     hv = {n: np_of(v[n]) for n in layers}
     hq = {n: np_of(q[n]) for n in layers}
     full_req = reqs[0]
-    if cid != 5:
-        shared_k, shared_slots_sub = _shared_page_view(w, lay, k)
-        P = w.P
-        mrow = lay.masked_rows[lay.masked_offsets[full_req]:lay.masked_offsets[full_req + 1]]
-        hq_full = np_of(q[:, torch.as_tensor(mrow.astype(np.int64), device=DEV)])
+    shared_k, shared_slots_sub = _shared_page_view(w, lay, k)
+    mrow = lay.masked_rows[lay.masked_offsets[full_req]:lay.masked_offsets[full_req + 1]]
+    hq_full = np_of(q[:, torch.as_tensor(mrow.astype(np.int64), device=DEV)])
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------ Part A
@@ -132,15 +129,16 @@ def test_full_size(cid):
     for b in range(w.batch):
         assert len(set(an[b].tolist())) == K and (np.diff(an[b]) > 0).all()
         assert an[b][0] >= w.affix_l and an[b][-1] < w.affix_l + w.L
-    if cid != 5:
-        say(f"anchor set of request {full_req} vs the oracle's full-layer scores")
-        s_full = O.probe_scores(hq_full, shared_k, shared_k, shared_slots_sub, w.page_size, w.n_kv_heads,
-                                np.arange(w.m), np.array([0, w.m]), scale)[0]
-        ok, exact = anchors_match(s_full, an[full_req], K, w.affix_l)
-        assert ok, "anchor set differs from the oracle beyond the tie band"
-        rel = np.abs(s_gpu[full_req] - s_full).max() / s_full.max()
-        assert rel <= 1e-3
-    del o_aff, lse, per_layer
+    say(f"anchor set of request {full_req} vs the oracle's full-layer scores")
+    s_full = O.probe_scores(hq_full, shared_k, shared_k, shared_slots_sub, w.page_size, w.n_kv_heads,
+                            np.arange(w.m), np.array([0, w.m]), scale)[0]
+    ok, exact = anchors_match(s_full, an[full_req], K, w.affix_l)
+    assert ok, "anchor set differs from the oracle beyond the tie band"
+    big = s_full >= 1e-6 * s_full.max()
+    rel = (np.abs(s_gpu[full_req] - s_full)[big] / s_full[big]).max()
+    assert rel <= 1e-3, f"request {full_req} scores rel err {rel}"
+    say(f"anchor set of request {full_req}: {'exact' if exact else 'within the tie band'}, scores rel err {rel:.2e}")
+    del o_aff, lse, per_layer, shared_k, hq_full
 
     # ------------------------------------------------------------ Part B
     say("seeded Top-K + maps")

@@ -44,7 +44,9 @@ def _check_chain(c, layers, fp32):
             assert ok, f"O_aff layer {n}: {st}"
         np.testing.assert_allclose(c.lse_aff[n].cpu().numpy(), c.r_lseaff[n], atol=1e-4 if not fp32 else 1e-5)
     if not exact_all:
-        pytest.skip("anchor sets agree only within the tie band; downstream stages are covered by the seeded tests")
+        # the sets differ only inside the tie band (checked above): the oracle's
+        # maps, scatter and attention are taken from the library's anchors
+        c.run_oracle_downstream(list(an), c.r_layers)
     assert np.array_equal(c.read_slot.cpu().numpy(), c.r_read)
     assert np.array_equal(c.rc_pos.cpu().numpy(), c.r_rcpos)
     assert np.array_equal(c.rc_slot.cpu().numpy(), c.r_rcslot)
@@ -702,11 +704,14 @@ def test_dropna_attention(idx):
     c.run_gpu()
     c.run_oracle()
     an = c.anchors.cpu().numpy()
+    for b in range(w.batch):
+        assert anchors_match(c.r_scores[b], an[b], c.K, w.affix_l)[0]
     if any(an[b].tolist() != c.r_anchors[b].tolist() for b in range(w.batch)):
-        pytest.skip("anchor sets agree only within the tie band")
+        # the sets differ only inside the tie band: the oracle's tables follow the library's anchors
+        c.run_oracle_downstream(list(an), c.r_layers)
     lay = c.lay
-    dn = [O.dropna_read_table(c.r_read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]], c.r_anchors[b], w.affix_l, w.L)
-          for b in range(w.batch)]
+    dn = [O.dropna_read_table(c.r_read[lay.kv_offsets[b]:lay.kv_offsets[b + 1]], c.r_anchors_used[b], w.affix_l,
+                              w.L) for b in range(w.batch)]
     assert np.array_equal(c.rc_slot.cpu().numpy(), np.concatenate(dn))
     out = torch.empty_like(c.qd)
     lse = torch.empty(c.qd.shape[:3], device=DEV)
@@ -809,8 +814,11 @@ def test_probe_full_normaliser_chain(idx):
             assert np.abs(got - of).max() <= 1e-5
         else:
             # three bf16 roundings stand between this output and the exact one (P inside each part,
-            # each part's O as stored, the merged O), one more than a single attention: 3 * 2^-9 * max|V|
-            ok, st = bf16_close(got, of, max_abs=3 * 2.0 ** -9 * 4.5)
+            # each part's O as stored, the merged O), one more than a single attention: up to
+            # 3 * 2^-9 * max|V|, which exceeds 2e-2 where an output nears the largest |V| (measured
+            # 0.0216 on this case); the one-pass formulation below holds the 2e-2 bar
+            vmax = float(np.abs(O.decode(hv[n])).max())
+            ok, st = bf16_close(got, of, max_abs=3 * 2.0 ** -9 * vmax)
             assert ok, f"full-normaliser O layer {n}: {st}"
         np.testing.assert_allclose(lse_aff[n].cpu().numpy(), lf, atol=1e-4)
     s_gpu = scores.cpu().numpy().astype(np.float64)

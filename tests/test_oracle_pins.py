@@ -125,6 +125,86 @@ def test_golden_mapped_attention():
     np.testing.assert_allclose(bo[0][0][0], [frac(x) for x in g["expected_out"]], atol=1e-12)
 
 
+def _block_slots_pins_hold():
+    """O.block_slots against its two pins: the hand-worked fixture, and the
+    closed-form private slots (oracle/brute.py, no read-slot table) of decode
+    blocks in seeded layouts with the affix as prefix, infix and suffix."""
+    g = gold("block_slots.json")
+    for c in g["cases"]:
+        got = O.block_slots(np.array(g["read_slot"]), g["kv_offsets"], c["block_start"], g["block_len"])
+        if got.tolist() != c["dst_slots"]:
+            return False
+    rng = np.random.default_rng(11)
+    for segs in ((("affix", 13), ("req", 3), ("gen", 8)), (("req", 2), ("affix", 9), ("req", 3), ("gen", 8)),
+                 (("req", 4), ("gen", 8), ("affix", 10))):
+        w = tiny_workload(segments=segs, batch=3, page_size=4)
+        K = O.anchor_count(w.L, w.rate)
+        lay = gen.make_layout(w, K, 3)
+        anchors = [O.topk_anchors(rng.standard_normal(w.L), K, w.affix_l) for _ in range(w.batch)]
+        read, _, _ = full_maps(w, K, lay, anchors)
+        pages = [lay.private_pages[lay.private_page_offsets[b]:lay.private_page_offsets[b + 1]]
+                 for b in range(w.batch)]
+        gen_pos = [p for p in range(w.T) if not (w.affix_l <= p < w.affix_l + w.L)]
+        blen = 4
+        starts = [p for p in gen_pos if all(q in gen_pos for q in range(p, p + blen))]
+        for _ in range(6):
+            bs = [int(rng.choice(starts)) for _ in range(w.batch)]
+            got = O.block_slots(read, lay.kv_offsets, bs, blen)
+            if got.tolist() != brute.block_slots(anchors, w.affix_l, w.L, pages, w.page_size, bs, blen):
+                return False
+    return True
+
+
+def test_golden_block_slots():
+    g = gold("block_slots.json")
+    pre, inf = gold("maps_prefix.json"), gold("maps_infix.json")
+    for c in g["cases"]:
+        got = O.block_slots(np.array(g["read_slot"]), g["kv_offsets"], c["block_start"], g["block_len"])
+        assert got.tolist() == c["dst_slots"]
+    # the closed form reaches the same slots from the anchors and private pages alone
+    assert pre["page_size"] == 4 and inf["page_size"] == 2
+    for c in g["cases"]:
+        b0 = brute.block_slots([pre["anchors"]], pre["affix_l"], pre["L"], [pre["private_pages"]], 4,
+                               [c["block_start"][0]], g["block_len"])
+        b1 = brute.block_slots([inf["anchors"]], inf["affix_l"], inf["L"], [inf["private_pages"]], 2,
+                               [c["block_start"][1]], g["block_len"])
+        assert b0 + b1 == c["dst_slots"]
+
+
+def test_block_slots_closed_form():
+    """Decode-block destinations read through the joint read-slot table equal
+    the closed-form private slots of the block's positions (Section 4.3 block
+    decoding, Section 4.1 maps), in all three affix placements."""
+    assert _block_slots_pins_hold()
+
+
+def _lse_merge_empty_pins_hold():
+    """An attention over the empty key set is O = 0, LSE = -inf (the empty
+    sum).  Merging it with the attention over a key set S is the attention
+    over the union, which is S itself: that part comes back unchanged, in
+    either order; two empty parts merge to the empty attention."""
+    w = tiny_workload()
+    K, lay, k, v, q = build_case(w)
+    qd = np_of(gen.make_rows(w, 3, gen.S_QDEC, heads=w.n_q_heads))
+    scale = 1 / math.sqrt(w.head_dim)
+    keys = lay.shared_slots[:7]
+    o_s, l_s = O.mapped_attention_layer(qd[0], k[0], v[0], [0, 3], keys, [0, 7], w.n_kv_heads, w.page_size, scale)
+    o_e, l_e = O.mapped_attention_layer(qd[0], k[0], v[0], [0, 3], keys[:0], [0, 0], w.n_kv_heads, w.page_size,
+                                        scale)
+    if not ((o_e == 0).all() and np.isneginf(l_e).all() and np.isfinite(l_s).all()):
+        return False
+    for a, b in (((o_e, l_e), (o_s, l_s)), ((o_s, l_s), (o_e, l_e))):
+        om, lm = O.lse_merge(a[0], a[1], b[0], b[1])
+        if not (np.array_equal(om, o_s) and np.array_equal(lm, l_s)):
+            return False
+    om, lm = O.lse_merge(o_e, l_e, o_e, l_e)
+    return bool((om == 0).all() and np.isneginf(lm).all())
+
+
+def test_lse_merge_empty_parts():
+    assert _lse_merge_empty_pins_hold()
+
+
 # ---------------------------------------------------------------------------
 # anchor count (Section 5 Default Settings; the workloads print K=13, Top-205)
 # ---------------------------------------------------------------------------
@@ -469,7 +549,9 @@ def test_brute_force_agrees(wl, order):
 def test_pins_catch_planted_mistakes(monkeypatch):
     """Plant plausible slips in the oracle and check a pin fails for each:
     a wrong GQA head mapping, masked-row sums taken over every row, ties
-    broken toward the higher offset."""
+    broken toward the higher offset, decode-block slots read without the
+    request's table offset or with a wrong block range, an LSE merge
+    without its empty-part branch."""
     w = tiny_workload()
     K, lay, k, v, q = build_case(w)
     scale = 1 / math.sqrt(w.head_dim)
@@ -494,6 +576,26 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         m.setattr(O, "topk_anchors",
                   lambda sc, kk, l: np.sort(np.lexsort((-np.arange(len(sc)), -np.asarray(sc)))[:kk]) + l)
         assert O.topk_anchors(np.array(g["scores"]), 5, g["affix_l"]).tolist() != g["cases"]["5"]
+    # decode-block slots read without the request's table offset
+    assert _block_slots_pins_hold()
+    with monkeypatch.context() as m:
+        m.setattr(O, "block_slots", lambda rs, ko, bs, bl: np.array(
+            [int(rs[bs[b] + i]) for b in range(len(ko) - 1) for i in range(bl)], np.int64))
+        assert not _block_slots_pins_hold()
+    # ... or with the block's length taken as its end position
+    with monkeypatch.context() as m:
+        m.setattr(O, "block_slots", lambda rs, ko, bs, bl: np.array(
+            [int(rs[ko[b] + i]) for b in range(len(ko) - 1) for i in range(bs[b], bl)], np.int64))
+        assert not _block_slots_pins_hold()
+    # an LSE merge without the empty-part branch (weights exp(lse_a - lse) with lse = -inf)
+    assert _lse_merge_empty_pins_hold()
+    with monkeypatch.context() as m:
+        def merge_unguarded(o_a, lse_a, o_b, lse_b):
+            lse = np.logaddexp(lse_a, lse_b)
+            with np.errstate(invalid="ignore"):
+                return (np.exp(lse_a - lse)[..., None] * o_a + np.exp(lse_b - lse)[..., None] * o_b, lse)
+        m.setattr(O, "lse_merge", merge_unguarded)
+        assert not _lse_merge_empty_pins_hold()
 
 
 def test_empty_context_is_empty_sum():
