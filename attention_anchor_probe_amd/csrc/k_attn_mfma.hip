@@ -395,42 +395,42 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // the direct-to-LDS tile loads are waited for explicitly (vmcnt) before it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// One 16-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
-// address lds_base + 16 * i.  Issued as asm so that the compiler does not
-// serialise later LDS reads behind it; callers wait on vmcnt themselves and
-// issue no other vector-memory loads whose results they consume meanwhile.
+// Direct-to-LDS loads through the compiler's builtins, which set M0 (the
+// wave-uniform LDS destination) themselves.  Lane i's bytes land at LDS byte
+// address lds_base + size * i.  The kernels wait for them on vmcnt
+// explicitly: the waits they need (a stage is read only after the wait and
+// barrier that follow its loads) are not data dependences the compiler sees.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+__device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(uintptr_t)a; }
+
+// 16 bytes per lane from a per-lane global address
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((gbl_void*)gptr, lds_ptr(lds_base), 16, 0, 0);
 }
 
-// The same with a scalar base and a 32-bit per-lane byte offset (saddr form:
-// no 64-bit address arithmetic per lane).
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+// 16 bytes per lane at byte offset voff of a buffer (a scalar base and
+// range): no 64-bit address arithmetic per lane, and an offset past the
+// range reads zeros instead of faulting
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds_base), 16, voff, 0, 0, 0);
 }
 
-// One 4-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
-// address lds_base + 4 * i (same waiting rules as dma16).
+// 4 bytes per lane from a per-lane global address
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((gbl_void*)gptr, lds_ptr(lds_base), 4, 0, 0);
 }
 
-// A wave-uniform pointer, asserted to the compiler so that it stays in scalar
-// registers (the scalar base of dma16s).
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const char*)(((uint64_t)hi << 32) | lo);
+// raw (unstrided) buffer resource over [base, base + bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
 // x on the lanes whose bit of `lanes` is clear, y on the others: one
-// v_cndmask with a scalar lane mask (the mask is built on the scalar unit)
+// v_cndmask with a scalar lane mask (the mask is built on the scalar unit;
+// the compiler keeps the wait states a matrix-unit result needs before it)
 __device__ __forceinline__ float select_lanes(float x, float y, uint64_t lanes) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "s"(lanes));
-  return r;
+  return __builtin_amdgcn_inverse_ballot_w64(lanes) ? y : x;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -458,6 +458,7 @@ struct TileSrc {
   const int32_t* table;
   int nk;
   const uint32_t* excl;  // EXCL only: bit j of excl[j / 32] set drops key j (padded to 64-key tiles)
+  uint32_t span;         // bytes readable from kbase + head_off (and vbase + head_off)
 };
 
 // Streams a key list through the workgroup's LDS in 64-key tiles into the
@@ -517,8 +518,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     kvx[i] = kchunk[i] ^ vchunk;
   }
   const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-  const char* kbase_s = uniform_ptr(src.kbase + src.head_off);
-  const char* vbase_s = uniform_ptr(src.vbase + src.head_off);
+  const __amdgpu_buffer_rsrc_t krs = byte_rsrc(src.kbase + src.head_off, src.span);
+  const __amdgpu_buffer_rsrc_t vrs = byte_rsrc(src.vbase + src.head_off, src.span);
   const uint32_t rmask = src.page_mask << 8;
   // K loads of a tile also record its row offsets (off, with the K chunk),
   // which its V loads reuse one iteration later
@@ -531,13 +532,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       // row offset below 2^32; the row part (bits 8..) and the chunk part
       // (bits 4..7) do not overlap
       off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
-      dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      dma16b(krs, off[i], st + 4 * i * ROWB);
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    for (int i = 0; i < 4; ++i) dma16b(vrs, off[i] ^ kvx[i], st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
@@ -572,11 +573,11 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
         s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
     if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
   };
-  // Scores of a tile are masked, and the running max updated (with the lazy
-  // rescale of O and the row sum), as soon as they are computed, at the end
-  // of the iteration before the one that takes their softmax: the body of an
-  // iteration (next scores, this tile's exponentials and P.V) is then free of
-  // branches, so the matrix and vector work of one wave can interleave.
+  // A tile's scores become its softmax weights as soon as they are computed,
+  // at the end of the iteration before the one that takes P.V: the body of an
+  // iteration (next scores, this tile's P.V, the next tile's exponentials) is
+  // then free of data-dependent branches, so the matrix and vector work of
+  // one wave can interleave.
   // EXCL: the tile's two exclusion words (one per 32-key half) are loaded
   // with vector loads two tiles ahead (a scalar load would have to wait for
   // every LDS read in flight) and taken into scalar registers after the wait
@@ -589,44 +590,68 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       }
     }
   };
-  auto settle = [&](f32x16* s, int tile, uint32_t e0, uint32_t e1) {
-    const int kb = tile * RB;
-    if constexpr (EXCL) {
-      // dropped keys (and the padding past the list) score -inf; lane half
-      // g2 holds keys 8*(i/4) + 4*g2 + i%4 of each 32-key half
-      if ((e0 | e1) != 0u) {
-        // element i of lane half g2 is key 8*(i/4) + 4*g2 + i%4: its bit for
-        // lanes 0..31 and lanes 32..63 forms a 64-bit lane mask
-        const float ninf = -INFINITY;
+  // Keys a tile must not count: EXCL, the dropped keys and the padding past
+  // the list (exclusion bits; applied to the scores on every tile, without a
+  // branch: most affix tiles hold an anchor); otherwise the keys of the last,
+  // partial tile past the end of the list (their rows repeat the list's last
+  // key, so their scores are finite).  Lane half g2 holds keys
+  // 8*(i/4) + 4*g2 + i%4 of each 32-key half.
+  auto excl_mask = [&](f32x16* s, uint32_t e0, uint32_t e1) {
+    // element i of lane half g2 is key 8*(i/4) + 4*g2 + i%4: its bit for
+    // lanes 0..31 and lanes 32..63 forms a 64-bit lane mask
+    const float ninf = -INFINITY;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const uint32_t w = sub ? e1 : e0;
+    for (int sub = 0; sub < 2; ++sub) {
+      const uint32_t w = sub ? e1 : e0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t k = 8 * (i >> 2) + (i & 3);
-            const uint32_t lo = 0u - ((w >> k) & 1u), hi = 0u - ((w >> (k + 4)) & 1u);
-            s[sub][i] = select_lanes(s[sub][i], ninf, ((uint64_t)hi << 32) | lo);
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t k = 8 * (i >> 2) + (i & 3);
+        const uint32_t lo = 0u - ((w >> k) & 1u), hi = 0u - ((w >> (k + 4)) & 1u);
+        s[sub][i] = select_lanes(s[sub][i], ninf, ((uint64_t)hi << 32) | lo);
       }
-    } else if (kb + RB > nk) {
+    }
+  };
+  auto past_end = [&](int tile, int sub, int i) { return tile * RB + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk; };
+  auto mask = [&](f32x16* s, int tile, uint32_t e0, uint32_t e1) {
+    if constexpr (EXCL) {
+      excl_mask(s, e0, e1);
+    } else if (tile * RB + RB > nk) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kb + sub * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3) >= nk) s[sub][i] = -INFINITY;
+          if (past_end(tile, sub, i)) s[sub][i] = -INFINITY;
     }
+  };
+  // weights P = 2^(s * c2 + nm) in place and this lane's sum of them (its 32
+  // keys of the tile), in four short chains
+  auto lane_sum = [&](const f32x16* s) -> float {
+    float ls[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = sub ? 0 : 4; i < 16; ++i) ls[i & 3] += s[sub][i];
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  auto expsum = [&](f32x16* s, float nm) -> float {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[sub][i] = fast_exp2(fmaf(s[sub][i], c2, nm));
+    return lane_sum(s);
+  };
+  // The exact step: the tile's max (both lane halves of a query), the
+  // running max raised to it when it is larger (O and the row sum rescaled
+  // by the same factor, so the result is exact either way), then the weights.
+  auto weigh_exact = [&](f32x16* s) -> float {
     float mr = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
-    mr = half_max(mr);
-    const float mt = mr * c2;
-    // rescale only when the running max grows by more than 2^8 (exact either
-    // way: O and the row sum carry the same factor)
-    if (mt > m + 8.f) {
-      const float alpha = exp2f(m - mt);
+    const float mt = half_max(mr) * c2;
+    if (mt > m) {
+      const float alpha = exp2f(m - mt);  // 0 while m is -inf (O and the sum are still 0)
       lsum *= alpha;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -634,24 +659,52 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
         for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
       m = mt;
     }
+    return expsum(s, m == -INFINITY ? 0.f : -m);
   };
-  // exponentials of a settled tile, its row sums and P.V
+  // Weights of a freshly scored tile against the running max as it stands
+  // (weigh_fast, in the iteration body, also past the last tile, where the
+  // weights are never used) and their check (weigh_check).  When every
+  // lane's sum stays at most 2^8 (so every weight does, as with a running max
+  // within 8 of the true one), the weights are kept; otherwise (a key above
+  // the running max by more than a factor 8 on average, or no finite running
+  // max yet: weights inf or NaN) the wave takes the exact step on scores
+  // recomputed from the tile, which is still in LDS.  No tile max is needed
+  // on the common path, and no branch stands before the exponentials: the
+  // last tile's keys past the end are zeroed after them.
+  auto weigh_fast = [&](f32x16* s, uint32_t e0, uint32_t e1) -> float {
+    if constexpr (EXCL) excl_mask(s, e0, e1);
+    const float ls = expsum(s, -m);
+    asm volatile("" ::"v"(ls));  // the weights and their sum belong to the iteration body
+    return ls;
+  };
+  auto weigh_check = [&](f32x16* s, int tile, float ls, uint32_t e0, uint32_t e1) {
+    if constexpr (!EXCL) {
+      if (tile * RB + RB > nk) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (past_end(tile, sub, i)) s[sub][i] = 0.f;
+        ls = lane_sum(s);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f)) != 0) {
+      scores(s, tile);
+      mask(s, tile, e0, e1);
+      ls = weigh_exact(s);
+    }
+    lsum += ls;
+  };
+  // P.V of a weighed tile: P rounded to bf16 as the A operand's partner
   auto absorb = [&](const f32x16* s, int tile) {
     const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
-    const float nm = (m == -INFINITY) ? 0.f : -m;
-    // fp32 row sums (the LSE feeds the column mass), in four short chains
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 pb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], c2, nm));
-          ls[j & 3] += pv;
-          pb[j] = (__bf16)pv;
-        }
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[sub][8 * hh + j];
         // V^T operand: key slots follow the score tile's C layout (keys
         // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
 #pragma unroll
@@ -662,10 +715,9 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
           o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
         }
       }
-    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
-  // one iteration: sc holds the settled scores of tile t, sn receives those
-  // of t+1; oc holds the row offsets of tile t+1, on receives those of t+2
+  // one iteration: sc holds the weights of tile t, sn receives those of
+  // t+1; oc holds the row offsets of tile t+1, on receives those of t+2
   // xc holds the exclusion words of tile t+1, xn receives those of t+2
   auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on, const uint32_t* xc,
                   uint32_t* xn) {
@@ -687,7 +739,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     // computing them keeps the body branch-free
     scores(sn, tile + 1);
     absorb(sc, tile);
-    if (tile + 1 < ntiles) settle(sn, tile + 1, f0, f1);
+    const float ls = weigh_fast(sn, f0, f1);
+    if (tile + 1 < ntiles) weigh_check(sn, tile + 1, ls, f0, f1);
   };
 
   f32x16 sa[2], sb[2];
@@ -708,7 +761,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     wg_barrier();
     if (live) {
       scores(sa, 0);
-      settle(sa, 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
+      mask(sa, 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
+      lsum += weigh_exact(sa);
     }
   }
   for (int tile = 0; tile < ntiles; tile += 2) {
@@ -828,6 +882,7 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   src.table = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
   src.nk = nk;
   src.excl = nullptr;
+  src.span = (uint32_t)(p.layer_bytes - src.head_off);
   tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   if constexpr (STORE) {
     // the request's fresh rows, read from the source (rows s0 .. s1 of this
@@ -845,6 +900,7 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
     fresh.table = nullptr;
     fresh.nk = s1 - s0;
     fresh.excl = nullptr;
+    fresh.span = (uint32_t)((size_t)fresh.nk * row_stride);
     wg_barrier();  // every wave is done with the stages of the first list
     tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   }
@@ -1014,6 +1070,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     src.table = p.kv_table;
     src.nk = p.n_kv;
     src.excl = p.excl + (size_t)min(b, p.B - 1) * p.excl_words;
+    src.span = (uint32_t)(p.layer_bytes - head_off);
     __builtin_amdgcn_s_setprio(1);  // ahead of the private phase's waves on the CU
     tile_loop<true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
     __builtin_amdgcn_s_setprio(0);
@@ -1028,6 +1085,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     const char* reg = smem + wave * (PTILE * ROWB * 2);  // K rows, then V rows
     const uint32_t kdst = lds_addr(reg), vdst = kdst + PTILE * ROWB;
     const int nt = (cnt + PTILE - 1) / PTILE;
+    const __amdgpu_buffer_rsrc_t krl = byte_rsrc(kbase, (uint32_t)p.layer_bytes);
+    const __amdgpu_buffer_rsrc_t vrl = byte_rsrc(vbase, (uint32_t)p.layer_bytes);
     int32_t ps[PTILE];
     // the lists are padded with valid slots to whole tiles
     auto pload = [&](int tile) {
@@ -1038,14 +1097,14 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     auto dma_k = [&]() {
 #pragma unroll
       for (int i = 0; i < PTILE / 4; ++i)
-        dma16(kbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
-              kdst + 4 * i * ROWB);
+        dma16b(krl, slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
+               kdst + 4 * i * ROWB);
     };
     auto dma_v = [&]() {
 #pragma unroll
       for (int i = 0; i < PTILE / 4; ++i)
-        dma16(vbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
-              vdst + 4 * i * ROWB);
+        dma16b(vrl, slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
+               vdst + 4 * i * ROWB);
     };
     pload(0);
     dma_k();

@@ -298,3 +298,47 @@ def test_hkvd_validation():
     assert hk(ss=None) == -1 and hk(s=None) == -1 and hk(kf=None) == -1
     assert hk(vf=FAKE_MIS) == -9
     assert hk(pool=pool(dtype=4)) == -2
+
+
+def test_only_the_c_abi_is_exported():
+    """The library's dynamic symbol table holds the acache_* calls and nothing
+    else (internal kernels, launchers and helpers stay local)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", Bd.LIB_PATH], capture_output=True, text=True, check=True)
+    names = [ln.split()[-1] for ln in out.stdout.splitlines() if ln.strip()]
+    assert names and all(n.startswith("acache_") for n in names), [n for n in names if not n.startswith("acache_")]
+    assert sorted(names) == declared()
+
+
+def test_check_slots_validation_and_workspace():
+    """Checked mode's pre-pass: sizes, modes, tables and workspace are checked
+    on the host before anything is launched; the workspace is 256 bytes for
+    reads and 256 + 4 per pool slot (rounded to 256) for writes."""
+    lib = Bd._lib()
+    nb = ctypes.c_size_t()
+    assert lib.acache_check_slots_workspace_bytes(8, 16, A.ACACHE_CHECK_READ, ctypes.byref(nb)) == 0
+    assert nb.value == 256
+    assert lib.acache_check_slots_workspace_bytes(8, 16, A.ACACHE_CHECK_WRITE, ctypes.byref(nb)) == 0
+    assert nb.value == 256 + 512
+    assert lib.acache_check_slots_workspace_bytes(100, 16, A.ACACHE_CHECK_WRITE, ctypes.byref(nb)) == 0
+    assert nb.value == 256 + 6400
+    assert lib.acache_check_slots_workspace_bytes(8, 12, 0, ctypes.byref(nb)) == -1     # page size not a power of 2
+    assert lib.acache_check_slots_workspace_bytes(8, 16, 2, ctypes.byref(nb)) == -1     # no such mode
+    assert lib.acache_check_slots_workspace_bytes(1 << 28, 16, 1, ctypes.byref(nb)) == -3  # more than 2^31 slots
+    bad = ctypes.c_int32(7)
+    # (slots, n, offsets, B, page_owner, n_pages, page_size, mode, bad, ws, ws_bytes, stream)
+    assert lib.acache_check_slots(FAKE, -1, None, 0, None, 8, 16, 0, ctypes.byref(bad), FAKE, 256, None) == -1
+    assert lib.acache_check_slots(None, 4, None, 0, None, 8, 16, 0, ctypes.byref(bad), FAKE, 256, None) == -1
+    assert lib.acache_check_slots(FAKE, 4, None, 2, None, 8, 16, 0, ctypes.byref(bad), FAKE, 256, None) == -1
+    assert lib.acache_check_slots(FAKE, 4, None, 0, None, 8, 16, 1, ctypes.byref(bad), FAKE, 256, None) == -7
+    assert lib.acache_check_slots(FAKE, 4, None, 0, None, 8, 16, 0, ctypes.byref(bad), None, 256, None) == -7
+    assert lib.acache_check_slots(FAKE, 4, None, 0, None, 8, 16, 0, ctypes.byref(bad), FAKE + 16, 256, None) == -7
+    assert bad.value == 7   # untouched on a host-side error
+    p = pool()
+    # (pool, k_src, v_src, dst, n_rows, row_offsets, B, page_owner, layer_begin, n_layers, bad, ws, ws_bytes, stream)
+    assert lib.acache_scatter_private_checked(ctypes.byref(p), FAKE, FAKE, FAKE, 4, FAKE, 1, FAKE, 0, 3,
+                                              ctypes.byref(bad), FAKE, 4096, None) == -1   # layer range
+    assert lib.acache_scatter_private_checked(ctypes.byref(p), FAKE_MIS, FAKE, FAKE, 4, FAKE, 1, FAKE, 0, 2,
+                                              ctypes.byref(bad), FAKE, 4096, None) == -9
+    assert lib.acache_scatter_private_checked(ctypes.byref(p), FAKE, FAKE, FAKE, 4, FAKE, 1, FAKE, 0, 2,
+                                              ctypes.byref(bad), FAKE, 512, None) == -7    # write mode needs 768
