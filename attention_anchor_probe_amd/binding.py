@@ -79,6 +79,11 @@ _SIG = {
     "acache_kv_footprint": ([_I, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64),
                              ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "acache_validate_slots": ([_P, _I, _P, _P, _I, _I, _I, ctypes.POINTER(_I)], ctypes.c_int),
+    "acache_check_slots_workspace_bytes": ([_I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "acache_check_slots": ([_P, _I, _P, _I, _P, _I, _I, _I, ctypes.POINTER(_I), _P, ctypes.c_size_t, _P],
+                           ctypes.c_int),
+    "acache_scatter_private_checked": ([ctypes.POINTER(KVPool), _P, _P, _P, _I, _P, _I, _P, _I, _I,
+                                        ctypes.POINTER(_I), _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIG)
 
@@ -259,6 +264,56 @@ def acache_scatter_private(pool_k, pool_v, k_src, v_src, dst_slots, layer_begin=
     st = _lib().acache_scatter_private(ctypes.byref(pool), _dev(k_src, pool_k.dtype), _dev(v_src, pool_k.dtype),
                                        _dev(dst_slots, torch.int32), n_rows, layer_begin, n_layers, _stream(stream))
     _check("acache_scatter_private", st)
+
+
+ACACHE_CHECK_READ, ACACHE_CHECK_WRITE = 0, 1
+
+
+def _check_ws(n_pages, page_size, mode, device, stream):
+    ws_bytes = ctypes.c_size_t()
+    _check("acache_check_slots_workspace_bytes",
+           _lib().acache_check_slots_workspace_bytes(int(n_pages), int(page_size), int(mode), ctypes.byref(ws_bytes)))
+    return _scratch(ws_bytes.value, device, stream)
+
+
+def acache_check_slots(slots, n_pages, page_size, mode, offsets=None, page_owner=None, workspace=None,
+                       stream=None):
+    """Checked mode's device pre-pass over a slot table.  Returns (status,
+    bad_index): status 0 (OK), or the first failing class ERANGE (-4),
+    EREGION (-5), EDUP (-6) with its smallest failing entry.  Other errors
+    raise AcacheError."""
+    B = offsets.numel() - 1 if offsets is not None else 0
+    if workspace is None:
+        workspace = _check_ws(n_pages, page_size, mode, slots.device, stream)
+    bad = _I(-2)
+    st = _lib().acache_check_slots(_dev(slots, torch.int32), slots.numel(), _dev(offsets, torch.int32), B,
+                                   _dev(page_owner, torch.int32), int(n_pages), int(page_size), int(mode),
+                                   ctypes.byref(bad), _dev(workspace), workspace.numel(), _stream(stream))
+    if st not in (0, -4, -5, -6):
+        _check("acache_check_slots", st)
+    return st, bad.value
+
+
+def acache_scatter_private_checked(pool_k, pool_v, k_src, v_src, dst_slots, row_offsets, page_owner, layer_begin=0,
+                                   workspace=None, stream=None):
+    """acache_scatter_private after the write-mode pre-pass: raises AcacheError
+    (status ERANGE / EREGION / EDUP, bad_index set) with the pool untouched
+    when a destination is out of range, outside its request's private pages
+    or repeated."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_rows = k_src.shape[0], k_src.shape[1]
+    B = row_offsets.numel() - 1
+    if workspace is None:
+        workspace = _check_ws(pool.n_pages, pool.page_size, ACACHE_CHECK_WRITE, pool_k.device, stream)
+    bad = _I(-2)
+    st = _lib().acache_scatter_private_checked(
+        ctypes.byref(pool), _dev(k_src, pool_k.dtype), _dev(v_src, pool_k.dtype), _dev(dst_slots, torch.int32),
+        n_rows, _dev(row_offsets, torch.int32), B, _dev(page_owner, torch.int32), layer_begin, n_layers,
+        ctypes.byref(bad), _dev(workspace), workspace.numel(), _stream(stream))
+    if st != 0:
+        err = AcacheError("acache_scatter_private_checked", st)
+        err.bad_index = bad.value
+        raise err
 
 
 def acache_block_slots(read_slot, kv_offsets, block_start, block_len, dst_slots, stream=None):

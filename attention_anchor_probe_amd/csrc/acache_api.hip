@@ -175,7 +175,8 @@ hipError_t probe_attention_launch(const acache_kv_pool* pool, const void* q, int
 }
 
 hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, int32_t n_rows,
-                                    const int32_t* masked_rows, const int32_t* masked_offsets, int32_t max_masked,
+                                    const int32_t* masked_rows, const int32_t* masked_offsets, int32_t n_masked,
+                                    int32_t max_masked,
                                     const int32_t* shared_slots, int32_t L, int32_t B, int32_t n_q_heads,
                                     int32_t layer_begin, int32_t n_layers, float scale, const float* lse,
                                     float* scores, float* partial, hipStream_t s, bool dry = false) {
@@ -186,6 +187,7 @@ hipError_t probe_column_mass_launch(const acache_kv_pool* pool, const void* q, i
   c.geo = geom_of(pool);
   c.masked_rows = masked_rows;
   c.masked_offsets = masked_offsets;
+  c.n_masked = n_masked;
   c.max_masked = max_masked;
   c.shared_slots = shared_slots;
   c.L = L;
@@ -244,11 +246,11 @@ int acache_probe_column_mass(const acache_kv_pool* pool, const void* q, int32_t 
   if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & (kAlign - 1)))
     return ACACHE_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots,
+  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, n_masked, max_masked, shared_slots,
                                                L, B, n_q_heads, layer_begin, n_layers, scale, lse_aff, scores,
                                                (float*)workspace, s, true))))
     return st;
-  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots, L,
+  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, n_masked, max_masked, shared_slots, L,
                                             B, n_q_heads, layer_begin, n_layers, scale, lse_aff, scores,
                                             (float*)workspace, s));
 }
@@ -282,14 +284,14 @@ int acache_probe_scores(const acache_kv_pool* pool, const void* q, int32_t n_row
   if ((st = limits_of(probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers,
                                              scale, o_aff, lse, s, true))))
     return st;
-  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots,
+  if ((st = limits_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, n_masked, max_masked, shared_slots,
                                                L, B, n_q_heads, layer_begin, n_layers, scale, lse, scores, (float*)ws,
                                                s, true))))
     return st;
   hipError_t e = probe_attention_launch(pool, q, n_rows, shared_slots, L, n_q_heads, layer_begin, n_layers, scale,
                                         o_aff, lse, s);
   if (e != hipSuccess) return ACACHE_EDEVICE;
-  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, max_masked, shared_slots, L,
+  return status_of(probe_column_mass_launch(pool, q, n_rows, masked_rows, masked_offsets, n_masked, max_masked, shared_slots, L,
                                             B, n_q_heads, layer_begin, n_layers, scale, lse, scores, (float*)ws, s));
 }
 
@@ -663,6 +665,62 @@ int acache_kv_footprint(int32_t B, const int32_t* seq_len, int32_t L, int32_t K,
   *private_bytes = priv * page;
   *dense_bytes = dense * page;
   return ACACHE_OK;
+}
+
+int acache_check_slots_workspace_bytes(int32_t n_pages, int32_t page_size, int32_t mode, size_t* bytes) {
+  if (!bytes || n_pages <= 0 || page_size <= 0 || (page_size & (page_size - 1))) return ACACHE_EINVAL;
+  if (mode != ACACHE_CHECK_READ && mode != ACACHE_CHECK_WRITE) return ACACHE_EINVAL;
+  const int64_t n_slots = (int64_t)n_pages * page_size;
+  if (n_slots > INT32_MAX) return ACACHE_ESHAPE;
+  *bytes = kAlign + (mode == ACACHE_CHECK_WRITE ? align_up((size_t)n_slots * sizeof(int32_t)) : 0);
+  return ACACHE_OK;
+}
+
+int acache_check_slots(const int32_t* slots, int32_t n, const int32_t* offsets, int32_t B,
+                       const int32_t* page_owner, int32_t n_pages, int32_t page_size, int32_t mode,
+                       int32_t* bad_index, void* workspace, size_t workspace_bytes, acache_stream_t stream) {
+  size_t need = 0;
+  int st;
+  if ((st = acache_check_slots_workspace_bytes(n_pages, page_size, mode, &need))) return st;
+  if (n < 0 || B < 0) return ACACHE_EINVAL;
+  if ((n > 0 && !slots) || (B > 0 && !offsets)) return ACACHE_EINVAL;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & (kAlign - 1))) return ACACHE_EWORKSPACE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  int32_t* rec = (int32_t*)workspace;
+  int32_t* first = mode == ACACHE_CHECK_WRITE ? (int32_t*)((char*)workspace + kAlign) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_check_slots(slots, n, B > 0 ? offsets : nullptr, B, page_owner,
+                                    (int64_t)n_pages * page_size, shift, mode == ACACHE_CHECK_WRITE, rec, first, s);
+  if (e != hipSuccess) return ACACHE_EDEVICE;
+  int32_t h[3];
+  if (hipMemcpyAsync(h, rec, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess) return ACACHE_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return ACACHE_EDEVICE;
+  static const int cls[3] = {ACACHE_ERANGE, ACACHE_EREGION, ACACHE_EDUP};
+  for (int c = 0; c < 3; ++c)
+    if (h[c] != INT32_MAX) {
+      if (bad_index) *bad_index = h[c];
+      return cls[c];
+    }
+  return ACACHE_OK;
+}
+
+int acache_scatter_private_checked(const acache_kv_pool* pool, const void* k_src, const void* v_src,
+                                   const int32_t* dst_slots, int32_t n_rows, const int32_t* row_offsets, int32_t B,
+                                   const int32_t* page_owner, int32_t layer_begin, int32_t n_layers,
+                                   int32_t* bad_index, void* workspace, size_t workspace_bytes,
+                                   acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if ((st = check_layers(pool, layer_begin, n_layers))) return st;
+  if (n_rows < 0) return ACACHE_EINVAL;
+  if (n_rows > 0 && (!k_src || !v_src || !dst_slots)) return ACACHE_EINVAL;
+  if (n_rows > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
+  if (n_layers > 65535) return ACACHE_ESHAPE;
+  if ((st = acache_check_slots(dst_slots, n_rows, row_offsets, B, page_owner, pool->n_pages, pool->page_size,
+                               ACACHE_CHECK_WRITE, bad_index, workspace, workspace_bytes, stream)))
+    return st;
+  return acache_scatter_private(pool, k_src, v_src, dst_slots, n_rows, layer_begin, n_layers, stream);
 }
 
 int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner, const int32_t* page_owner,

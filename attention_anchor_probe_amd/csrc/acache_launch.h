@@ -70,6 +70,7 @@ struct ColmassArgs {
   PoolGeom geo;
   const int32_t* masked_rows;
   const int32_t* masked_offsets;
+  int n_masked;    // entries of masked_rows
   int max_masked;
   const int32_t* shared_slots;
   int L;
@@ -110,6 +111,13 @@ constexpr int kStorePlanMaxKv = 1 << 18;
 hipError_t launch_store_plan(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* src_pos,
                              const int32_t* src_offsets, int B, int max_kv, int stride, int32_t* other_slots,
                              int32_t* other_counts, hipStream_t st);
+// Checked mode: the pre-pass over a slot table (k_check.hip).  rec[0..2]
+// receive the smallest failing entry of ERANGE, EREGION and EDUP (INT32_MAX:
+// none); first is n_slots int32 of scratch in write mode.
+hipError_t launch_check_slots(const int32_t* slots, int n, const int32_t* offsets, int B,
+                              const int32_t* page_owner, int64_t n_slots, int page_shift, int write_mode,
+                              int32_t* rec, int32_t* first, hipStream_t stream);
+
 hipError_t launch_block_slots(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* block_start,
                               int B, int block_len, int32_t* dst, hipStream_t st);
 hipError_t launch_scatter(void* pool_k, void* pool_v, const void* k_src, const void* v_src, const int32_t* dst,

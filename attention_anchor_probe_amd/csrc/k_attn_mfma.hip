@@ -100,6 +100,7 @@ struct ColP {
   PoolGeom geo;
   const int32_t* masked_rows;
   const int32_t* masked_offsets;
+  int n_masked;
   const int32_t* shared_slots;
   int L;
   int n_rows;
@@ -395,35 +396,36 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // the direct-to-LDS tile loads are waited for explicitly (vmcnt) before it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Direct-to-LDS loads through the compiler's builtins, which set M0 (the
-// wave-uniform LDS destination) themselves.  Lane i's bytes land at LDS byte
-// address lds_base + size * i.  The kernels wait for them on vmcnt
-// explicitly: the waits they need (a stage is read only after the wait and
-// barrier that follow its loads) are not data dependences the compiler sees.
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
-__device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(uintptr_t)a; }
-
-// 16 bytes per lane from a per-lane global address
+// Direct-to-LDS loads.  Lane i's bytes land at LDS byte address
+// lds_base + size * i; M0 holds lds_base, passed to the instruction as an
+// operand (the compiler sets it).  They are issued as asm: the compiler's
+// wait insertion would treat a load into one LDS stage as a store that every
+// later LDS read must wait for, also the reads of the other stage.  The
+// kernels wait for these loads on vmcnt explicitly (a stage is read only
+// after the wait and barrier that follow its loads), and every load whose
+// result they consume is waited for after such an explicit wait.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)gptr, lds_ptr(lds_base), 16, 0, 0);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
-// 16 bytes per lane at byte offset voff of a buffer (a scalar base and
-// range): no 64-bit address arithmetic per lane, and an offset past the
-// range reads zeros instead of faulting
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds_base), 16, voff, 0, 0, 0);
+// the same with a scalar base and a 32-bit per-lane byte offset (saddr form:
+// no 64-bit address arithmetic per lane)
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
 // 4 bytes per lane from a per-lane global address
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)gptr, lds_ptr(lds_base), 4, 0, 0);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
-// raw (unstrided) buffer resource over [base, base + bytes)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+// A wave-uniform pointer, asserted to the compiler so that it stays in scalar
+// registers (the scalar base of dma16s).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
 }
 
 // x on the lanes whose bit of `lanes` is clear, y on the others: one
@@ -458,7 +460,6 @@ struct TileSrc {
   const int32_t* table;
   int nk;
   const uint32_t* excl;  // EXCL only: bit j of excl[j / 32] set drops key j (padded to 64-key tiles)
-  uint32_t span;         // bytes readable from kbase + head_off (and vbase + head_off)
 };
 
 // Streams a key list through the workgroup's LDS in 64-key tiles into the
@@ -466,9 +467,10 @@ struct TileSrc {
 // accumulators o) of this wave's 32 query rows, whose Q fragments are qf.
 // Every wave of the workgroup calls it: the tile loads are shared, and
 // waves with live == false only help load.
-template <bool EXCL, bool CONTIG = false>
-__device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[8],
-                                          bool live, int wave, int lane, float& m, float& lsum, f32x16 (&o)[4]) {
+template <bool EXCL, bool CONTIG = false, int NB = 1>
+__device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[NB][8],
+                                          bool live, int wave, int lane, float (&m)[NB], float (&lsum)[NB],
+                                          f32x16 (&o)[NB][4]) {
   const int nk = src.nk;
   const int ntiles = (nk + RB - 1) / RB;
   const int g2 = lane >> 5, l32 = lane & 31;
@@ -518,8 +520,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     kvx[i] = kchunk[i] ^ vchunk;
   }
   const uint32_t lds0 = lds_addr(smem) + 16 * wave * ROWB;
-  const __amdgpu_buffer_rsrc_t krs = byte_rsrc(src.kbase + src.head_off, src.span);
-  const __amdgpu_buffer_rsrc_t vrs = byte_rsrc(src.vbase + src.head_off, src.span);
+  const char* kbase_s = uniform_ptr(src.kbase + src.head_off);
+  const char* vbase_s = uniform_ptr(src.vbase + src.head_off);
   const uint32_t rmask = src.page_mask << 8;
   // K loads of a tile also record its row offsets (off, with the K chunk),
   // which its V loads reuse one iteration later
@@ -532,13 +534,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       // row offset below 2^32; the row part (bits 8..) and the chunk part
       // (bits 4..7) do not overlap
       off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
-      dma16b(krs, off[i], st + 4 * i * ROWB);
+      dma16s(kbase_s, off[i], st + 4 * i * ROWB);
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16b(vrs, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
@@ -555,10 +557,10 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
   }
 
-  auto scores = [&](f32x16* s, int tile) {
+  auto scores = [&](f32x16 (*s)[2], int tile) {
     const char* st = smem + (tile & 1) * KSTAGE;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) s[bl][0] = s[bl][1] = f32x16{};
     // the two 32-key halves alternate, so that two independent accumulation
     // chains share the matrix pipe.  In the shared-affix decode (EXCL), where
     // workgroups in the memory-bound private phase share the CU, the shared
@@ -569,8 +571,12 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+      for (int sub = 0; sub < 2; ++sub) {
+        // one K fragment read serves every row block of the wave
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB));
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) s[bl][sub] = mfma(kf, qf[bl][c], s[bl][sub]);
+      }
     if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
   };
   // A tile's scores become its softmax weights as soon as they are computed,
@@ -643,23 +649,23 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // The exact step: the tile's max (both lane halves of a query), the
   // running max raised to it when it is larger (O and the row sum rescaled
   // by the same factor, so the result is exact either way), then the weights.
-  auto weigh_exact = [&](f32x16* s) -> float {
+  auto weigh_exact = [&](f32x16* s, int bl) -> float {
     float mr = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
     const float mt = half_max(mr) * c2;
-    if (mt > m) {
-      const float alpha = exp2f(m - mt);  // 0 while m is -inf (O and the sum are still 0)
-      lsum *= alpha;
+    if (mt > m[bl]) {
+      const float alpha = exp2f(m[bl] - mt);  // 0 while m is -inf (O and the sum are still 0)
+      lsum[bl] *= alpha;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
-      m = mt;
+        for (int i = 0; i < 16; ++i) o[bl][a][i] *= alpha;
+      m[bl] = mt;
     }
-    return expsum(s, m == -INFINITY ? 0.f : -m);
+    return expsum(s, m[bl] == -INFINITY ? 0.f : -m[bl]);
   };
   // Weights of a freshly scored tile against the running max as it stands
   // (weigh_fast, in the iteration body, also past the last tile, where the
@@ -671,56 +677,106 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // recomputed from the tile, which is still in LDS.  No tile max is needed
   // on the common path, and no branch stands before the exponentials: the
   // last tile's keys past the end are zeroed after them.
-  auto weigh_fast = [&](f32x16* s, uint32_t e0, uint32_t e1) -> float {
-    if constexpr (EXCL) excl_mask(s, e0, e1);
-    const float ls = expsum(s, -m);
-    asm volatile("" ::"v"(ls));  // the weights and their sum belong to the iteration body
-    return ls;
+  // the weights in bf16, the operand of P.V: pw[bl][sub][hh] holds keys
+  // 16*hh + (the C layout's eight per lane) of 32-key half sub
+  auto to_bf16 = [&](const f32x16 (*s)[2], bf16x8 (*pw)[2][2]) {
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pw[bl][sub][hh][j] = (__bf16)s[bl][sub][8 * hh + j];
   };
-  auto weigh_check = [&](f32x16* s, int tile, float ls, uint32_t e0, uint32_t e1) {
+  auto weigh_fast = [&](f32x16 (*s)[2], bf16x8 (*pw)[2][2], float* ls, uint32_t e0, uint32_t e1) {
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) {
+      if constexpr (EXCL) excl_mask(s[bl], e0, e1);
+      ls[bl] = expsum(s[bl], -m[bl]);
+      asm volatile("" ::"v"(ls[bl]));  // the weights and their sum belong to the iteration body
+    }
+    to_bf16(s, pw);
+  };
+  auto weigh_check = [&](f32x16 (*s)[2], bf16x8 (*pw)[2][2], int tile, float* ls, uint32_t e0, uint32_t e1) {
     if constexpr (!EXCL) {
       if (tile * RB + RB > nk) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int bl = 0; bl < NB; ++bl) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (past_end(tile, sub, i)) s[sub][i] = 0.f;
-        ls = lane_sum(s);
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (past_end(tile, sub, i)) s[bl][sub][i] = 0.f;
+          ls[bl] = lane_sum(s[bl]);
+        }
+        to_bf16(s, pw);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f)) != 0) {
+    bool redo = false;
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) redo = redo || !(ls[bl] <= 256.f);
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
       scores(s, tile);
-      mask(s, tile, e0, e1);
-      ls = weigh_exact(s);
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        mask(s[bl], tile, e0, e1);
+        ls[bl] = weigh_exact(s[bl], bl);
+      }
+      to_bf16(s, pw);
     }
-    lsum += ls;
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) lsum[bl] += ls[bl];
   };
   // P.V of a weighed tile: P rounded to bf16 as the A operand's partner
-  auto absorb = [&](const f32x16* s, int tile) {
+  auto absorb = [&](const bf16x8 (*pw)[2][2], int tile) {
     const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[sub][8 * hh + j];
         // V^T operand: key slots follow the score tile's C layout (keys
-        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing reads
+        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing
+        // reads, which serve every row block of the wave
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl) o[bl][a] = mfma(vf, pw[bl][sub][hh], o[bl][a]);
         }
       }
   };
-  // one iteration: sc holds the weights of tile t, sn receives those of
-  // t+1; oc holds the row offsets of tile t+1, on receives those of t+2
+  // Instruction order of the iteration body (the compiler keeps each LDS
+  // read next to the MFMA that takes it, so every MFMA would wait out a whole
+  // LDS latency): the score MFMAs of tile t+1, each K fragment read four
+  // MFMA groups ahead; then the P.V MFMAs of tile t, each group with its two
+  // transposing V reads four groups ahead and a share of tile t+1's scale
+  // products, exponentials, sums and bf16 conversions.
+  auto pipeline_body = [&]() {
+    constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, NB, 0);
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);  // the first V reads
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, NB, 0);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 7 * NB, 0);
+    }
+  };
+  // one iteration: pc holds the bf16 weights of tile t, pn receives those of
+  // t+1; oc holds the row offsets of tile t+1, on receives those of t+2;
   // xc holds the exclusion words of tile t+1, xn receives those of t+2
-  auto step = [&](int tile, f32x16* sc, f32x16* sn, const uint32_t* oc, uint32_t* on, const uint32_t* xc,
-                  uint32_t* xn) {
+  f32x16 sn[NB][2];
+  auto step = [&](int tile, const bf16x8 (*pc)[2][2], bf16x8 (*pn)[2][2], const uint32_t* oc, uint32_t* on,
+                  const uint32_t* xc, uint32_t* xn) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
     wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
     uint32_t f0 = 0, f1 = 0;
@@ -738,12 +794,14 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     // past the last tile the scores read a stale stage and are never used;
     // computing them keeps the body branch-free
     scores(sn, tile + 1);
-    absorb(sc, tile);
-    const float ls = weigh_fast(sn, f0, f1);
-    if (tile + 1 < ntiles) weigh_check(sn, tile + 1, ls, f0, f1);
+    absorb(pc, tile);
+    float ls[NB];
+    weigh_fast(sn, pn, ls, f0, f1);
+    if constexpr (NB == 1) pipeline_body();
+    if (tile + 1 < ntiles) weigh_check(sn, pn, tile + 1, ls, f0, f1);
   };
 
-  f32x16 sa[2], sb[2];
+  bf16x8 pa[NB][2][2], pb[NB][2][2];
   uint32_t oa[4], ob[4];
   uint32_t xa[2] = {0u, 0u}, xb[2] = {0u, 0u};
   if (ntiles > 0) {
@@ -760,14 +818,18 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     __builtin_amdgcn_s_waitcnt(0x3F70);
     wg_barrier();
     if (live) {
-      scores(sa, 0);
-      mask(sa, 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
-      lsum += weigh_exact(sa);
+      scores(sn, 0);
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        mask(sn[bl], 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
+        lsum[bl] += weigh_exact(sn[bl], bl);
+      }
+      to_bf16(sn, pa);
     }
   }
   for (int tile = 0; tile < ntiles; tile += 2) {
-    step(tile, sa, sb, oa, ob, xa, xb);
-    if (tile + 1 < ntiles) step(tile + 1, sb, sa, ob, oa, xb, xa);
+    step(tile, pa, pb, oa, ob, xa, xb);
+    if (tile + 1 < ntiles) step(tile + 1, pb, pa, ob, oa, xb, xa);
   }
 }
 
@@ -779,7 +841,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
 // those rows of their (layer, KV head) to the pool, a slice per row tile; the
 // call reads no slot it writes, so the copy needs no ordering against the
 // attention.
-template <bool STORE>
+template <bool STORE, int NB = 1>
 __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
@@ -839,38 +901,49 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   }
   const int nq = q1 - q0;
   const int rows = packed ? p.gpack * nq : nq;  // rows of this (request, head or group)
-  const int rbase = t * 128;
+  const int rbase = t * (128 * NB);
   if (rbase >= rows) return;
   const int nk = k1 - k0;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, l32 = lane & 31;
-  const int lrow = rbase + wave * 32 + l32;
-  const bool qvalid = lrow < rows;
-  const bool wave_live = rbase + wave * 32 < rows;
-  // this lane's query row and head (rows >= 1 here, so nq >= 1); lanes past
-  // the rows take the first row and head of the unit, whose Q they load but
-  // whose results they never store
-  int qrow = q0 + (qvalid ? lrow : 0), h = hu;
-  if (packed) {
-    const int j = qvalid ? lrow / nq : 0;
-    qrow = q0 + (qvalid ? lrow - j * nq : 0);
-    h = g * p.gpack + j;
-  }
-
+  // this wave holds rows rbase + 32 * NB * wave + 32 * bl + l32 (row block bl)
+  const int wrow = rbase + 32 * NB * wave;
+  const bool wave_live = wrow < rows;
+  int qrow[NB], h[NB];
+  bool qvalid[NB];
   // Q as the B operand of S^T = K Q^T
-  bf16x8 qf[8];
-  {
-    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D + g2 * 8;
+  bf16x8 qf[NB][8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  for (int bl = 0; bl < NB; ++bl) {
+    const int lrow = wrow + 32 * bl + l32;
+    qvalid[bl] = lrow < rows;
+    // this lane's query row and head (rows >= 1 here, so nq >= 1); lanes past
+    // the rows take the first row and head of the unit, whose Q they load but
+    // whose results they never store
+    qrow[bl] = q0 + (qvalid[bl] ? lrow : 0);
+    h[bl] = hu;
+    if (packed) {
+      const int j = qvalid[bl] ? lrow / nq : 0;
+      qrow[bl] = q0 + (qvalid[bl] ? lrow - j * nq : 0);
+      h[bl] = g * p.gpack + j;
+    }
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow[bl]) * p.n_q_heads + h[bl]) * D + g2 * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      qf[bl][c] = qvalid[bl] ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x16 o[4];
+  float m[NB], lsum[NB];
+  f32x16 o[NB][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) o[a] = f32x16{};
+  for (int bl = 0; bl < NB; ++bl) {
+    m[bl] = -INFINITY;
+    lsum[bl] = 0.f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) o[bl][a] = f32x16{};
+  }
 
   TileSrc src;
   src.kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
@@ -882,8 +955,7 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   src.table = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
   src.nk = nk;
   src.excl = nullptr;
-  src.span = (uint32_t)(p.layer_bytes - src.head_off);
-  tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+  tile_loop<false, false, NB>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   if constexpr (STORE) {
     // the request's fresh rows, read from the source (rows s0 .. s1 of this
     // layer and KV head, one row stride apart)
@@ -900,28 +972,31 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
     fresh.table = nullptr;
     fresh.nk = s1 - s0;
     fresh.excl = nullptr;
-    fresh.span = (uint32_t)((size_t)fresh.nk * row_stride);
     wg_barrier();  // every wave is done with the stages of the first list
-    tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    tile_loop<false, true, NB>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   }
-  const float lt = half_sum(lsum);
-  if (!qvalid) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (p.out) {
-    bf16_t* op = p.out + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int bl = 0; bl < NB; ++bl) {
+    const float lt = half_sum(lsum[bl]);
+    if (!qvalid[bl]) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const size_t row = ((size_t)n * p.n_q + qrow[bl]) * p.n_q_heads + h[bl];
+    if (p.out) {
+      bf16_t* op = p.out + row * D;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = a * 32 + 8 * i4 + 4 * g2;
-        u32x2 w;
-        w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
-        w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
-        *(u32x2*)(op + d) = w;
-      }
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = a * 32 + 8 * i4 + 4 * g2;
+          const f32x16& oa = o[bl][a];
+          u32x2 w;
+          w[0] = (uint32_t)f32_to_bf16(oa[4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(oa[4 * i4 + 1] * inv) << 16);
+          w[1] = (uint32_t)f32_to_bf16(oa[4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(oa[4 * i4 + 3] * inv) << 16);
+          *(u32x2*)(op + d) = w;
+        }
+    }
+    if (p.lse && g2 == 0) p.lse[row] = lt > 0.f ? (m[bl] + log2f(lt)) * kLn2 : -INFINITY;
   }
-  if (p.lse && g2 == 0)
-    p.lse[((size_t)n * p.n_q + qrow) * p.n_q_heads + h] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
@@ -971,8 +1046,9 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   const bool qvalid = qrow < q1;
   const bool wave_live = q1 > q0;
 
-  // Q as the B operand of S^T = K Q^T
-  bf16x8 qf[8];
+  // Q as the B operand of S^T = K Q^T (one row block per wave)
+  bf16x8 qf1[1][8];
+  bf16x8 (&qf)[8] = qf1[0];
   {
     const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : 0)) * p.n_q_heads + h) * D + g2 * 8;
 #pragma unroll
@@ -980,8 +1056,10 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   }
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x16 o[4];
+  float m1[1] = {-INFINITY}, lsum1[1] = {0.f};
+  float &m = m1[0], &lsum = lsum1[0];
+  f32x16 o1[1][4];
+  f32x16 (&o)[4] = o1[0];
 #pragma unroll
   for (int a = 0; a < 4; ++a) o[a] = f32x16{};
 
@@ -1070,9 +1148,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     src.table = p.kv_table;
     src.nk = p.n_kv;
     src.excl = p.excl + (size_t)min(b, p.B - 1) * p.excl_words;
-    src.span = (uint32_t)(p.layer_bytes - head_off);
     __builtin_amdgcn_s_setprio(1);  // ahead of the private phase's waves on the CU
-    tile_loop<true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    tile_loop<true>(smem, src, p.c2, qf1, wave_live, wave, lane, m1, lsum1, o1);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -1085,8 +1162,6 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     const char* reg = smem + wave * (PTILE * ROWB * 2);  // K rows, then V rows
     const uint32_t kdst = lds_addr(reg), vdst = kdst + PTILE * ROWB;
     const int nt = (cnt + PTILE - 1) / PTILE;
-    const __amdgpu_buffer_rsrc_t krl = byte_rsrc(kbase, (uint32_t)p.layer_bytes);
-    const __amdgpu_buffer_rsrc_t vrl = byte_rsrc(vbase, (uint32_t)p.layer_bytes);
     int32_t ps[PTILE];
     // the lists are padded with valid slots to whole tiles
     auto pload = [&](int tile) {
@@ -1097,14 +1172,14 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     auto dma_k = [&]() {
 #pragma unroll
       for (int i = 0; i < PTILE / 4; ++i)
-        dma16b(krl, slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
-               kdst + 4 * i * ROWB);
+        dma16(kbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
+              kdst + 4 * i * ROWB);
     };
     auto dma_v = [&]() {
 #pragma unroll
       for (int i = 0; i < PTILE / 4; ++i)
-        dma16b(vrl, slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
-               vdst + 4 * i * ROWB);
+        dma16(vbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
+              vdst + 4 * i * ROWB);
     };
     pload(0);
     dma_k();
@@ -1225,21 +1300,29 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   // the row's global chunk kswz(row, lane%16).
   const int ra = 8 * wave + (lane >> 4);  // tile rows this lane moves: ra, ra + 4
   const uint32_t gchunk0 = kswz(ra, lane & 15) * 16, gchunk1 = kswz(ra + 4, lane & 15) * 16;
-  const char* qhead = (const char*)(p.q + ((size_t)n * p.n_rows * p.n_q_heads + h) * D);
-  const size_t qrow_bytes = (size_t)p.n_q_heads * D * sizeof(bf16_t);
+  // one layer and head of Q from a scalar base: a row's bytes start at
+  // row * qrow_bytes (below 2^32, rows and row bytes below 2^24: checked at launch)
+  const char* qhead = uniform_ptr((const char*)(p.q + ((size_t)n * p.n_rows * p.n_q_heads + h) * D));
+  const uint32_t qrow_bytes = (uint32_t)p.n_q_heads * D * sizeof(bf16_t);
   const uint32_t lds_q = lds_addr(&Qs[0][0]) + 8 * wave * ROWB;
-  // masked-row indices of a tile: the two rows this lane moves
+  // masked-row indices of a tile: the two rows this lane moves, read through
+  // a buffer over masked_rows (the tile's first row in the scalar offset).
+  // Rows past the request's last masked row take whatever row follows (the
+  // next request's, or row 0 past the end of the list, where the buffer
+  // reads zero): a valid row whose accumulator start is -inf, weight 0.
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.masked_rows, (short)0, p.n_masked * 4, 0x00020000);
   struct RowIdx { int ra, rb; };
   auto rows_load = [&](It t) -> RowIdx {
     RowIdx ix;
-    ix.ra = p.masked_rows[min(t.r0 + ra, t.m1 - 1)];
-    ix.rb = p.masked_rows[min(t.r0 + ra + 4, t.m1 - 1)];
+    ix.ra = __builtin_amdgcn_raw_buffer_load_b32(mrs, ra * 4, t.r0 * 4, 0);
+    ix.rb = __builtin_amdgcn_raw_buffer_load_b32(mrs, ra * 4 + 16, t.r0 * 4, 0);
     return ix;
   };
   auto dma_q = [&](int stage, const RowIdx& ix) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_q + stage * (32 * ROWB));
-    dma16(qhead + (size_t)ix.ra * qrow_bytes + gchunk0, dst);
-    dma16(qhead + (size_t)ix.rb * qrow_bytes + gchunk1, dst + 4 * ROWB);
+    dma16s(qhead, __umul24((uint32_t)ix.ra, qrow_bytes) + gchunk0, dst);
+    dma16s(qhead, __umul24((uint32_t)ix.rb, qrow_bytes) + gchunk1, dst + 4 * ROWB);
   };
   // the tile's 32 prepared accumulator starts (-inf past the request's
   // rows, so they add exp2(-inf) = 0), moved by lanes 0..31 of wave 0
@@ -1357,9 +1440,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   const int B = a.q_offsets ? a.B : 1;
   const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
   const bool split = G == 0 && a.max_q <= 32;
-  const int RT = split ? 32 : 128;
   if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
   const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
+  const int RT = split ? 32 : 128;
   AttnP p{};
   p.q = (const bf16_t*)a.q;
   p.pool_k = (const bf16_t*)a.pool_k;
@@ -1481,6 +1564,7 @@ hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_ru
   p.geo = a.geo;
   p.masked_rows = a.masked_rows;
   p.masked_offsets = a.masked_offsets;
+  p.n_masked = a.n_masked;
   p.shared_slots = a.shared_slots;
   p.L = a.L;
   p.n_rows = a.n_rows;
@@ -1493,6 +1577,10 @@ hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_ru
   p.lse_prep = a.lse_prep;
   p.lse_stride = a.lse_stride;
   p.key_blocks = (a.L + 255) / 256;
+  // Q rows are addressed with 32-bit offsets and 24-bit products
+  const long long qrow_bytes = (long long)a.n_q_heads * D * 2;
+  if (a.n_rows >= (1 << 24) || qrow_bytes >= (1 << 24) || (long long)a.n_rows * qrow_bytes >= (1ll << 32))
+    return hipErrorInvalidValue;
   const long long units = (long long)a.n_layers * a.n_q_heads * p.key_blocks;
   if (units == 0) return hipSuccess;
   if (units > (1ll << 30)) return hipErrorInvalidValue;

@@ -24,8 +24,11 @@
  *  - Return value: ACACHE_OK (0) or a negative status.  Scalar, shape,
  *    alignment and pointer checks run on the host before anything is
  *    enqueued, so an error return means nothing was launched.  Table
- *    *contents* (slot ids, offsets) are trusted; acache_validate_slots checks
- *    host copies of them.  A kernel launch failure returns ACACHE_EDEVICE.
+ *    *contents* (slot ids, offsets) are trusted by the compute calls; the
+ *    checked mode checks them first: acache_check_slots (a device pre-pass,
+ *    synchronous) and acache_scatter_private_checked (that pre-pass, then
+ *    the scatter only when it passes), or acache_validate_slots on host
+ *    copies.  A kernel launch failure returns ACACHE_EDEVICE.
  *  - Element types: Q, the pool, scatter sources and attention outputs share
  *    the pool's dtype (ACACHE_F32 or ACACHE_BF16); scores and LSE are fp32;
  *    indices and offsets are int32.  Vector pointers must be 16-byte aligned.
@@ -56,9 +59,9 @@ enum acache_status {
   ACACHE_EINVAL = -1,     /* null pointer, bad scalar (rate, K, scale, layer range) */
   ACACHE_EDTYPE = -2,     /* unknown dtype */
   ACACHE_ESHAPE = -3,     /* unsupported head_dim / page_size / head grouping / size limit */
-  ACACHE_ERANGE = -4,     /* slot or index out of range (acache_validate_slots) */
-  ACACHE_EREGION = -5,    /* scatter destination outside the request's private pages */
-  ACACHE_EDUP = -6,       /* duplicate scatter destination */
+  ACACHE_ERANGE = -4,     /* slot or index out of range (checked mode, acache_validate_slots) */
+  ACACHE_EREGION = -5,    /* slot outside the region its request may read or write (checked mode) */
+  ACACHE_EDUP = -6,       /* duplicate scatter destination (checked mode) */
   ACACHE_EWORKSPACE = -7, /* workspace missing or too small */
   ACACHE_EDEVICE = -8,    /* HIP launch error */
   ACACHE_EALIGN = -9      /* pointer not 16-byte aligned */
@@ -417,6 +420,61 @@ int acache_kv_footprint(int32_t B, const int32_t* seq_len /*host*/, int32_t L, i
 int acache_validate_slots(const int32_t* slots, int32_t n, const int32_t* owner,
                           const int32_t* page_owner, int32_t n_pages, int32_t page_size,
                           int32_t distinct, int32_t* bad_index);
+
+/*
+ * Checked mode: a device pre-pass over a slot table (Section 4.1: requests
+ * read the shared region and their own private slots and write only their
+ * own private slots; Appendix C.1: the store writes through the write-side
+ * map before the read-slot kernel reads through the read-slot map).
+ *
+ *  slots       [n] physical slots (device); segment b is
+ *              slots[offsets[b] .. offsets[b+1]), request b's entries
+ *  offsets     [B+1] (device), nullable with B = 0: one segment with no
+ *              request (a table of the shared region, such as shared_slots)
+ *  page_owner  [n_pages] (device), nullable: -1 shared page, b private to
+ *              request b, -2 free.  Without it only ranges and duplicates
+ *              are checked
+ *  mode        ACACHE_CHECK_READ: every slot in range and, with page_owner,
+ *              in a shared page or a page of its own segment's request (one
+ *              segment without offsets: shared pages only);
+ *              ACACHE_CHECK_WRITE: every slot in range, with page_owner in a
+ *              page of its own segment's request (without offsets: of some
+ *              request), and no slot named twice over all segments
+ *  bad_index   (host, nullable) receives the smallest failing entry of the
+ *              class returned (-1: the offsets table itself)
+ *  workspace   >= acache_check_slots_workspace_bytes(n_pages, page_size,
+ *              mode) bytes, 256-B aligned (4 bytes per pool slot in write
+ *              mode)
+ * Returns the first failing class in this order: ERANGE (a slot outside
+ * [0, n_pages * page_size), or offsets not rising from 0 to n), EREGION,
+ * EDUP; else OK.  The pre-pass reads the tables, offsets and page owners,
+ * never the pool.  The call waits for the stream (it reads the result back),
+ * so it cannot be captured in a graph.  EINVAL for bad sizes, a NULL table
+ * or mode; EWORKSPACE for a missing or short workspace.
+ */
+enum acache_check_mode { ACACHE_CHECK_READ = 0, ACACHE_CHECK_WRITE = 1 };
+
+int acache_check_slots_workspace_bytes(int32_t n_pages, int32_t page_size, int32_t mode,
+                                       size_t* bytes /*host*/);
+
+int acache_check_slots(const int32_t* slots, int32_t n, const int32_t* offsets, int32_t B,
+                       const int32_t* page_owner, int32_t n_pages, int32_t page_size, int32_t mode,
+                       int32_t* bad_index, void* workspace, size_t workspace_bytes,
+                       acache_stream_t stream);
+
+/*
+ * acache_scatter_private in checked mode (Section 4.1, Section 4.3,
+ * Appendix C.1): the write-mode pre-pass of acache_check_slots over dst_slots
+ * (row_offsets [B+1] assigns rows to requests; page_owner as above), then the
+ * scatter only when it passes.  On ERANGE, EREGION or EDUP nothing is
+ * written to the pool.  Same arguments as acache_scatter_private plus those
+ * of the check; waits for the stream like acache_check_slots.
+ */
+int acache_scatter_private_checked(const acache_kv_pool* pool, const void* k_src, const void* v_src,
+                                   const int32_t* dst_slots, int32_t n_rows, const int32_t* row_offsets,
+                                   int32_t B, const int32_t* page_owner, int32_t layer_begin,
+                                   int32_t n_layers, int32_t* bad_index, void* workspace,
+                                   size_t workspace_bytes, acache_stream_t stream);
 
 #if defined(__GNUC__)
 #pragma GCC visibility pop
