@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     acache_probe_attention, acache_probe_column_mass_workspace_bytes, acache_probe_column_mass,
     acache_topk_anchors, acache_build_maps, acache_scatter_private, acache_block_slots,
     acache_mapped_attention, acache_mapped_attention_shared_workspace_bytes, acache_mapped_attention_shared,
+    acache_mapped_attention_shared_noalloc,
     acache_store_attend_workspace_bytes, acache_store_attend,
     acache_hkvd_scores, acache_lse_merge, acache_kv_footprint, acache_validate_slots,
     ACACHE_CHECK_READ, ACACHE_CHECK_WRITE, acache_check_slots, acache_scatter_private_checked,

@@ -70,6 +70,8 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "acache_mapped_attention_shared": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                         _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "acache_mapped_attention_shared_noalloc": ([ctypes.POINTER(KVPool), _P, _P, _I, _I, _P, _P, _I, _P, _I, _I, _I,
+                                                _I, _I, _I, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "acache_store_attend_workspace_bytes": ([ctypes.POINTER(KVPool), _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
                                             ctypes.c_int),
     "acache_store_attend": ([ctypes.POINTER(KVPool), _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
@@ -382,6 +384,26 @@ def acache_mapped_attention_shared(pool_k, pool_v, q, q_offsets, read_slot, kv_o
         _dev(workspace) if workspace is not None else None, workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("acache_mapped_attention_shared", st)
+
+
+def acache_mapped_attention_shared_noalloc(pool_k, pool_v, q, q_offsets, read_slot, kv_offsets, shared_slots, out,
+                                           *, affix_l, max_q_per_req, max_kv_per_req, lse=None, layer_begin=0,
+                                           scale=None, stream=None):
+    """acache_mapped_attention_shared without a workspace: the library keeps
+    the plan in its fixed per-GPU scratch array (calls on one GPU must not
+    overlap; a plan beyond the array's size raises EWORKSPACE)."""
+    pool = make_pool(pool_k, pool_v)
+    n_layers, n_q, hq, d = q.shape
+    B = q_offsets.numel() - 1
+    L = shared_slots.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib().acache_mapped_attention_shared_noalloc(
+        ctypes.byref(pool), _dev(q, pool_k.dtype), _dev(q_offsets, torch.int32), n_q, int(max_q_per_req),
+        _dev(read_slot, torch.int32), _dev(kv_offsets, torch.int32), int(max_kv_per_req),
+        _dev(shared_slots, torch.int32), int(affix_l), L, B, hq, layer_begin, n_layers, float(scale),
+        _dev(out, pool_k.dtype), _dev(lse, torch.float32), _stream(stream))
+    _check("acache_mapped_attention_shared_noalloc", st)
 
 
 def acache_store_attend_workspace_bytes(pool_k, pool_v, *, B, max_q_per_req, max_kv_per_req):

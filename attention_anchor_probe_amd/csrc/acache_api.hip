@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "acache_dev.h"
@@ -513,6 +514,57 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                     (uint32_t*)(ws + w.excl), w.excl_words, s);
   if (e != hipSuccess) return status_of(e);
   return status_of(launch_attn_mfma_shared(a, s));
+}
+
+}  // extern "C"
+
+namespace {
+// The allocation-free shared-affix call keeps its plan (each request's other
+// read slots, their counts, the affix exclusion bits) in this fixed device
+// array.  Every GPU the library runs on holds its own copy until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// reports for the current device, taken once per device.
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (set up on its first use there)
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ACACHE_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ACACHE_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ACACHE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const void* q, const int32_t* q_offsets,
+                                           int32_t n_q, int32_t max_q_per_req, const int32_t* read_slot,
+                                           const int32_t* kv_offsets, int32_t max_kv_per_req,
+                                           const int32_t* shared_slots, int32_t affix_l, int32_t L, int32_t B,
+                                           int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
+                                           void* out, float* lse, acache_stream_t stream) {
+  int st;
+  if ((st = check_pool(pool))) return st;
+  if (B < 0 || n_q < 0 || max_q_per_req < 0 || n_q_heads < 0 || n_layers < 0 || max_kv_per_req < 0 || L < 0)
+    return ACACHE_EINVAL;
+  const SharedWs w = shared_ws_layout(pool, B, n_q, max_q_per_req, n_q_heads, n_layers, max_kv_per_req, L);
+  if (w.total > kScratchBytes) return ACACHE_EWORKSPACE;  // the plan does not fit the fixed scratch
+  void* ws = nullptr;
+  if (w.total > 0 && (st = scratch_of_current_device(&ws))) return st;
+  return acache_mapped_attention_shared(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets,
+                                        max_kv_per_req, shared_slots, affix_l, L, B, n_q_heads, layer_begin,
+                                        n_layers, scale, out, lse, ws, w.total, stream);
 }
 
 }  // extern "C"

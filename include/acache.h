@@ -18,9 +18,10 @@
  *    call returns.  Scratch memory comes from a caller workspace whose size
  *    the matching *_workspace_bytes query reports.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *    stream) and return after enqueueing.  They hold no mutable global state;
- *    calls on different streams may run concurrently when their outputs do
- *    not overlap.
+ *    stream) and return after enqueueing.  They hold no mutable global state
+ *    (acache_mapped_attention_shared_noalloc aside: it keeps one fixed scratch
+ *    array per GPU); calls on different streams may run concurrently when
+ *    their outputs do not overlap.
  *  - Return value: ACACHE_OK (0) or a negative status.  Scalar, shape,
  *    alignment and pointer checks run on the host before anything is
  *    enqueued, so an error return means nothing was launched.  Table
@@ -306,6 +307,26 @@ int acache_mapped_attention_shared(const acache_kv_pool* pool, const void* q, co
                                    int32_t n_q_heads, int32_t layer_begin, int32_t n_layers, float scale,
                                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                                    acache_stream_t stream);
+
+/*
+ * acache_mapped_attention_shared for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and result, without the workspace: the plan lives in a fixed
+ * device array of the library, 8 MiB on each GPU it runs on (held until the
+ * process ends), taken on the current device (hipGetDevice; the stream must
+ * belong to it).  The call allocates nothing.  A call whose plan needs more
+ * than 8 MiB (the size acache_mapped_attention_shared_workspace_bytes reports
+ * for the same arguments) returns EWORKSPACE with nothing enqueued.  Every
+ * call on one GPU shares the array: calls that overlap on one GPU (other
+ * streams, or other host threads) race and must not be issued.
+ */
+int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const void* q,
+                                           const int32_t* q_offsets, int32_t n_q, int32_t max_q_per_req,
+                                           const int32_t* read_slot, const int32_t* kv_offsets,
+                                           int32_t max_kv_per_req, const int32_t* shared_slots,
+                                           int32_t affix_l, int32_t L, int32_t B, int32_t n_q_heads,
+                                           int32_t layer_begin, int32_t n_layers, float scale, void* out,
+                                           float* lse, acache_stream_t stream);
 
 /*
  * Store-then-attend of the recompute phase, Section 4.3 and Appendix C.1:
