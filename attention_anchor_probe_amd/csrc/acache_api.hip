@@ -425,8 +425,10 @@ SharedWs shared_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t n_q, in
   SharedWs w;
   // a decode block whose query-head groups fill a row tile when packed is
   // MFMA-bound: the single-pass call (which packs them) then serves it
-  // better than the shared-affix kernel, whose gain is HBM reads
-  w.two_pass = mfma_supported(pool->dtype, pool->head_dim) && max_q <= 32 &&
+  // better than the shared-affix kernel, whose gain is HBM reads.  A batch of
+  // one request reads the affix once either way, and the single pass (its
+  // keys split over four waves) fills the CU better
+  w.two_pass = mfma_supported(pool->dtype, pool->head_dim) && max_q <= 32 && B >= 2 &&
                gqa_pack(n_q_heads, pool->n_kv_heads, max_q) == 0;
   if (!w.two_pass) return w;
   w.excl_words = 2 * ((L + 63) / 64);

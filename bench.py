@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--ceilings", action="store_true",
                     help="also time a large library bf16 GEMM and torch's fused attention at the probe's per-layer "
                          "shape on the same GPU: context for the probe kernel's MFMA rate, not part of the path")
+    ap.add_argument("--shared-slot-order", choices=("page", "slot"), default=None,
+                    help="order of the shared region's slots: whole pages (the workloads' default) or a slot-granular "
+                         "shuffle, the worst case for the read-slot attention's gathers")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     return ap.parse_args()
@@ -528,6 +531,8 @@ def main():
         sys.exit(2)
     dev = "cuda:0"
     w = WORKLOADS[args.workload]
+    if args.shared_slot_order and args.shared_slot_order != w.shared_slot_order:
+        w = w.scaled(shared_slot_order=args.shared_slot_order, name=f"{w.name}-{args.shared_slot_order}-granular")
     S = Setup(w, dev)
     progress(f"inputs of {w.name} resident")
     host = None
@@ -622,14 +627,13 @@ def main():
     else:
         map_kernels = ("shared_plan_kernel", "attn_shared_mfma")
         roof_kernel = "read-slot attention, one shared-affix call for all layers (" + " + ".join(map_kernels) + ")"
-    map_traffic = [traffic.get(k) for k in map_kernels]
+    map_traffic = [traffic.get(k) for k in (("attn_rows_mfma:read_slot",) if mapped_mfma else map_kernels)]
     roof_mapped = {"kernel": roof_kernel, "bound": "mfma" if mapped_mfma else "hbm",
                    "achieved": mapped_tflops if mapped_mfma else mapped_gbs,
                    "peak": PEAK_BF16_TFLOPS if mapped_mfma else PEAK_HBM_GBS,
                    "unit": "TFLOP/s" if mapped_mfma else "GB/s",
                    "frac": mapped_tflops / PEAK_BF16_TFLOPS if mapped_mfma else mapped_gbs / PEAK_HBM_GBS,
-                   "traffic": (sum(map_traffic) if all(t is not None for t in map_traffic) else None)
-                   if not mapped_mfma else None,
+                   "traffic": sum(map_traffic) if all(t is not None for t in map_traffic) else None,
                    "traffic_unit": "HBM bytes per call", "algorithmic_per_launch":
                    wm["mapped_flops"] if mapped_mfma else wm["mapped_bytes"],
                    "algorithmic_bytes_per_launch": wm["mapped_bytes"], "algorithmic_gbs": mapped_gbs}
@@ -641,13 +645,19 @@ def main():
         "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "affix_L": w.L, "affix_at": w.affix_l, "request_tokens": w.P - w.m,
                    "gen_tokens": w.m, "batch": w.batch, "anchor_rate": w.rate, "K": S.K, "decode_block": w.block_len,
-                   "logical_len": w.T, "page_size": w.page_size, "page_order": w.page_order},
+                   "logical_len": w.T, "page_size": w.page_size, "page_order": w.page_order,
+                   "shared_slot_order": w.shared_slot_order},
         "mapped_attention_pct_bf16_peak": 100.0 * mapped_tflops / PEAK_BF16_TFLOPS,
         "kv_footprint_gb": {"shared": fp["shared"] / 1e9, "private": fp["private"] / 1e9,
                             "dense": fp["dense"] / 1e9,
                             "acache_saving": 1 - (fp["shared"] + fp["private"]) / fp["dense"]},
         "probe_ms_per_request": probe_ms_req,
         "probe_attention_tflops": probe_tflops,
+        # the probe's algorithmic bytes (affix K/V once, Q, O_aff, LSE) over its time: with few rows per request
+        # (one request at L=1024) the probe sits near the ridge, so both fractions are reported
+        "probe_attention_hbm": {"achieved": wm["probe_bytes"] / t_probe / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": wm["probe_bytes"] / t_probe / 1e9 / PEAK_HBM_GBS,
+                                "algorithmic_bytes_per_launch": wm["probe_bytes"]},
         "admission_scatter_gbs": scatter_gbs,
         "stage_ms": stage_ms,
         "stage_ms_p10": stage_pct[10],

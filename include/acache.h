@@ -284,11 +284,12 @@ int acache_mapped_attention(const acache_kv_pool* pool, const void* q, const int
  * Any read table gives the same result as acache_mapped_attention (up to fp32
  * summation order); the gain needs most affix positions routed to
  * shared_slots, as the maps of acache_build_maps / acache_topk_anchors do.
- * Decode blocks (max_q_per_req <= 32) of bf16 pools with head_dim 128 take
- * the two-pass path, unless each KV head serves G > 1 query heads with
- * G * max_q_per_req >= 128 (then the work is bound by the matrix units, not by
- * HBM reads); every other case runs acache_mapped_attention itself, with no
- * workspace needed (the size query returns 0).
+ * Decode blocks (max_q_per_req <= 32) of bf16 pools with head_dim 128 and
+ * batches of B >= 2 requests take the two-pass path, unless each KV head
+ * serves G > 1 query heads with G * max_q_per_req >= 128 (then the work is
+ * bound by the matrix units, not by HBM reads); every other case runs
+ * acache_mapped_attention itself, with no workspace needed (the size query
+ * returns 0).
  * Requests must satisfy T_b <= max_kv_per_req (positions past it are not
  * read).  The workspace (size from the query below, given the same pool,
  * B, n_q, max_q_per_req, n_q_heads, n_layers, max_kv_per_req and L) holds

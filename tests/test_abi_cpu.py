@@ -152,9 +152,10 @@ def test_shared_attention_validation_and_workspace():
     assert ws(p, 32, mkv=200) > need and ws(p, 32, L=64000) > need
     assert ws(p, 33) == 0                        # more than 32 rows per request: single-pass path
     assert ws(pool(dtype=0, head_dim=64), 32) == 0
+    assert _ws_query(lib, p, 1, 32, 32, 4, 2, 100, 64) == 0   # one request: single-pass path
     at = lambda **kw: lib.acache_mapped_attention_shared(
         ctypes.byref(kw.pop("pool", p)), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE,
-        kw.get("mkv", 100), kw.get("ss", FAKE), kw.get("al", 0), kw.get("L", 64), kw.get("B", 1), kw.get("hq", 4),
+        kw.get("mkv", 100), kw.get("ss", FAKE), kw.get("al", 0), kw.get("L", 64), kw.get("B", 2), kw.get("hq", 4),
         0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, kw.get("ws", FAKE * 16), kw.get("wsb", 1 << 24),
         None)
     assert at(B=0) == 0
