@@ -125,6 +125,13 @@ __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *(const u32x4*)p
 // toward zero, which is harmless for softmax weights; exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -362,8 +369,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
       }
       const int d = a * 32 + 8 * i4 + 4 * g2;
       u32x2 wv;
-      wv[0] = (uint32_t)f32_to_bf16(v4[0]) | ((uint32_t)f32_to_bf16(v4[1]) << 16);
-      wv[1] = (uint32_t)f32_to_bf16(v4[2]) | ((uint32_t)f32_to_bf16(v4[3]) << 16);
+      wv[0] = pack_bf16x2(v4[0], v4[1]);
+      wv[1] = pack_bf16x2(v4[2], v4[3]);
       *(u32x2*)(op + d) = wv;
     }
   }
@@ -467,10 +474,9 @@ struct TileSrc {
 // accumulators o) of this wave's 32 query rows, whose Q fragments are qf.
 // Every wave of the workgroup calls it: the tile loads are shared, and
 // waves with live == false only help load.
-template <bool EXCL, bool CONTIG = false, int NB = 1>
-__device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[NB][8],
-                                          bool live, int wave, int lane, float (&m)[NB], float (&lsum)[NB],
-                                          f32x16 (&o)[NB][4]) {
+template <bool EXCL, bool CONTIG = false>
+__device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[8],
+                                          bool live, int wave, int lane, float& m, float& lsum, f32x16 (&o)[4]) {
   const int nk = src.nk;
   const int ntiles = (nk + RB - 1) / RB;
   const int g2 = lane >> 5, l32 = lane & 31;
@@ -557,10 +563,9 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
   }
 
-  auto scores = [&](f32x16 (*s)[2], int tile) {
+  auto scores = [&](f32x16* s, int tile) {
     const char* st = smem + (tile & 1) * KSTAGE;
-#pragma unroll
-    for (int bl = 0; bl < NB; ++bl) s[bl][0] = s[bl][1] = f32x16{};
+    s[0] = s[1] = f32x16{};
     // the two 32-key halves alternate, so that two independent accumulation
     // chains share the matrix pipe.  In the shared-affix decode (EXCL), where
     // workgroups in the memory-bound private phase share the CU, the shared
@@ -572,10 +577,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        // one K fragment read serves every row block of the wave
-        const bf16x8 kf = as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB));
-#pragma unroll
-        for (int bl = 0; bl < NB; ++bl) s[bl][sub] = mfma(kf, qf[bl][c], s[bl][sub]);
+        s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
       }
     if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
   };
@@ -649,23 +651,23 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // The exact step: the tile's max (both lane halves of a query), the
   // running max raised to it when it is larger (O and the row sum rescaled
   // by the same factor, so the result is exact either way), then the weights.
-  auto weigh_exact = [&](f32x16* s, int bl) -> float {
+  auto weigh_exact = [&](f32x16* s) -> float {
     float mr = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
     const float mt = half_max(mr) * c2;
-    if (mt > m[bl]) {
-      const float alpha = exp2f(m[bl] - mt);  // 0 while m is -inf (O and the sum are still 0)
-      lsum[bl] *= alpha;
+    if (mt > m) {
+      const float alpha = exp2f(m - mt);  // 0 while m is -inf (O and the sum are still 0)
+      lsum *= alpha;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[bl][a][i] *= alpha;
-      m[bl] = mt;
+        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+      m = mt;
     }
-    return expsum(s, m[bl] == -INFINITY ? 0.f : -m[bl]);
+    return expsum(s, m == -INFINITY ? 0.f : -m);
   };
   // Weights of a freshly scored tile against the running max as it stands
   // (weigh_fast, in the iteration body, also past the last tile, where the
@@ -677,59 +679,44 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // recomputed from the tile, which is still in LDS.  No tile max is needed
   // on the common path, and no branch stands before the exponentials: the
   // last tile's keys past the end are zeroed after them.
-  // the weights in bf16, the operand of P.V: pw[bl][sub][hh] holds keys
+  // the weights in bf16, the operand of P.V: pw[sub][hh] holds keys
   // 16*hh + (the C layout's eight per lane) of 32-key half sub
-  auto to_bf16 = [&](const f32x16 (*s)[2], bf16x8 (*pw)[2][2]) {
+  auto to_bf16 = [&](const f32x16* s, bf16x8 (*pw)[2]) {
 #pragma unroll
-    for (int bl = 0; bl < NB; ++bl)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pw[bl][sub][hh][j] = (__bf16)s[bl][sub][8 * hh + j];
+        for (int j = 0; j < 8; ++j) pw[sub][hh][j] = (__bf16)s[sub][8 * hh + j];
   };
-  auto weigh_fast = [&](f32x16 (*s)[2], bf16x8 (*pw)[2][2], float* ls, uint32_t e0, uint32_t e1) {
-#pragma unroll
-    for (int bl = 0; bl < NB; ++bl) {
-      if constexpr (EXCL) excl_mask(s[bl], e0, e1);
-      ls[bl] = expsum(s[bl], -m[bl]);
-      asm volatile("" ::"v"(ls[bl]));  // the weights and their sum belong to the iteration body
-    }
+  auto weigh_fast = [&](f32x16* s, bf16x8 (*pw)[2], float& ls, uint32_t e0, uint32_t e1) {
+    if constexpr (EXCL) excl_mask(s, e0, e1);
+    ls = expsum(s, -m);
+    asm volatile("" ::"v"(ls));  // the weights and their sum belong to the iteration body
     to_bf16(s, pw);
   };
-  auto weigh_check = [&](f32x16 (*s)[2], bf16x8 (*pw)[2][2], int tile, float* ls, uint32_t e0, uint32_t e1) {
+  auto weigh_check = [&](f32x16* s, bf16x8 (*pw)[2], int tile, float ls, uint32_t e0, uint32_t e1) {
     if constexpr (!EXCL) {
       if (tile * RB + RB > nk) {
 #pragma unroll
-        for (int bl = 0; bl < NB; ++bl) {
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (past_end(tile, sub, i)) s[bl][sub][i] = 0.f;
-          ls[bl] = lane_sum(s[bl]);
-        }
+          for (int i = 0; i < 16; ++i)
+            if (past_end(tile, sub, i)) s[sub][i] = 0.f;
+        ls = lane_sum(s);
         to_bf16(s, pw);
       }
     }
-    bool redo = false;
-#pragma unroll
-    for (int bl = 0; bl < NB; ++bl) redo = redo || !(ls[bl] <= 256.f);
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!(ls <= 256.f)) != 0) {
       scores(s, tile);
-#pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        mask(s[bl], tile, e0, e1);
-        ls[bl] = weigh_exact(s[bl], bl);
-      }
+      mask(s, tile, e0, e1);
+      ls = weigh_exact(s);
       to_bf16(s, pw);
     }
-#pragma unroll
-    for (int bl = 0; bl < NB; ++bl) lsum[bl] += ls[bl];
+    lsum += ls;
   };
   // P.V of a weighed tile: P rounded to bf16 as the A operand's partner
-  auto absorb = [&](const bf16x8 (*pw)[2][2], int tile) {
+  auto absorb = [&](const bf16x8 (*pw)[2], int tile) {
     const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -737,15 +724,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       for (int hh = 0; hh < 2; ++hh) {
         // V^T operand: key slots follow the score tile's C layout (keys
         // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing
-        // reads, which serve every row block of the wave
+        // reads
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int bl = 0; bl < NB; ++bl) o[bl][a] = mfma(vf, pw[bl][sub][hh], o[bl][a]);
+          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pw[sub][hh], o[a]);
         }
       }
   };
@@ -760,22 +745,21 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, NB, 0);
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-      else __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);  // the first V reads
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);  // K reads, then the first V reads
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, NB, 0);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       if (i < 14) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kValu, 7 * NB, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 7, 0);
     }
   };
   // one iteration: pc holds the bf16 weights of tile t, pn receives those of
   // t+1; oc holds the row offsets of tile t+1, on receives those of t+2;
   // xc holds the exclusion words of tile t+1, xn receives those of t+2
-  f32x16 sn[NB][2];
-  auto step = [&](int tile, const bf16x8 (*pc)[2][2], bf16x8 (*pn)[2][2], const uint32_t* oc, uint32_t* on,
+  f32x16 sn[2];
+  auto step = [&](int tile, const bf16x8 (*pc)[2], bf16x8 (*pn)[2], const uint32_t* oc, uint32_t* on,
                   const uint32_t* xc, uint32_t* xn) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1) and V(t) have landed
     wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
@@ -795,13 +779,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     // computing them keeps the body branch-free
     scores(sn, tile + 1);
     absorb(pc, tile);
-    float ls[NB];
+    float ls;
     weigh_fast(sn, pn, ls, f0, f1);
-    if constexpr (NB == 1) pipeline_body();
+    pipeline_body();
     if (tile + 1 < ntiles) weigh_check(sn, pn, tile + 1, ls, f0, f1);
   };
 
-  bf16x8 pa[NB][2][2], pb[NB][2][2];
+  bf16x8 pa[2][2], pb[2][2];
   uint32_t oa[4], ob[4];
   uint32_t xa[2] = {0u, 0u}, xb[2] = {0u, 0u};
   if (ntiles > 0) {
@@ -819,11 +803,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     wg_barrier();
     if (live) {
       scores(sn, 0);
-#pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        mask(sn[bl], 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
-        lsum[bl] += weigh_exact(sn[bl], bl);
-      }
+      mask(sn, 0, __builtin_amdgcn_readfirstlane(xb[0]), __builtin_amdgcn_readfirstlane(xb[1]));
+      lsum += weigh_exact(sn);
       to_bf16(sn, pa);
     }
   }
@@ -841,7 +822,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
 // those rows of their (layer, KV head) to the pool, a slice per row tile; the
 // call reads no slot it writes, so the copy needs no ordering against the
 // attention.
-template <bool STORE, int NB = 1>
+template <bool STORE>
 __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
@@ -901,49 +882,40 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   }
   const int nq = q1 - q0;
   const int rows = packed ? p.gpack * nq : nq;  // rows of this (request, head or group)
-  const int rbase = t * (128 * NB);
+  const int rbase = t * 128;
   if (rbase >= rows) return;
   const int nk = k1 - k0;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, l32 = lane & 31;
-  // this wave holds rows rbase + 32 * NB * wave + 32 * bl + l32 (row block bl)
-  const int wrow = rbase + 32 * NB * wave;
+  // this wave holds rows rbase + 32 * wave + l32
+  const int wrow = rbase + 32 * wave;
   const bool wave_live = wrow < rows;
-  int qrow[NB], h[NB];
-  bool qvalid[NB];
+  const int lrow = wrow + l32;
+  const bool qvalid = lrow < rows;
+  // this lane's query row and head (rows >= 1 here, so nq >= 1); lanes past
+  // the rows take the first row and head of the unit, whose Q they load but
+  // whose results they never store
+  int qrow = q0 + (qvalid ? lrow : 0), h = hu;
+  if (packed) {
+    const int j = qvalid ? lrow / nq : 0;
+    qrow = q0 + (qvalid ? lrow - j * nq : 0);
+    h = g * p.gpack + j;
+  }
   // Q as the B operand of S^T = K Q^T
-  bf16x8 qf[NB][8];
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow) * p.n_q_heads + h) * D + g2 * 8;
 #pragma unroll
-  for (int bl = 0; bl < NB; ++bl) {
-    const int lrow = wrow + 32 * bl + l32;
-    qvalid[bl] = lrow < rows;
-    // this lane's query row and head (rows >= 1 here, so nq >= 1); lanes past
-    // the rows take the first row and head of the unit, whose Q they load but
-    // whose results they never store
-    qrow[bl] = q0 + (qvalid[bl] ? lrow : 0);
-    h[bl] = hu;
-    if (packed) {
-      const int j = qvalid[bl] ? lrow / nq : 0;
-      qrow[bl] = q0 + (qvalid[bl] ? lrow - j * nq : 0);
-      h[bl] = g * p.gpack + j;
-    }
-    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow[bl]) * p.n_q_heads + h[bl]) * D + g2 * 8;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      qf[bl][c] = qvalid[bl] ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
-  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
+  // no wait here: the Q loads overlap the first tile loads, and the vmcnt(0)
+  // that closes the tile loop's prologue covers both
 
-  float m[NB], lsum[NB];
-  f32x16 o[NB][4];
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
 #pragma unroll
-  for (int bl = 0; bl < NB; ++bl) {
-    m[bl] = -INFINITY;
-    lsum[bl] = 0.f;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) o[bl][a] = f32x16{};
-  }
+  for (int a = 0; a < 4; ++a) o[a] = f32x16{};
 
   TileSrc src;
   src.kbase = (const char*)p.pool_k + (size_t)layer * p.layer_bytes;
@@ -955,7 +927,7 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   src.table = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
   src.nk = nk;
   src.excl = nullptr;
-  tile_loop<false, false, NB>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+  tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   if constexpr (STORE) {
     // the request's fresh rows, read from the source (rows s0 .. s1 of this
     // layer and KV head, one row stride apart)
@@ -973,30 +945,26 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
     fresh.nk = s1 - s0;
     fresh.excl = nullptr;
     wg_barrier();  // every wave is done with the stages of the first list
-    tile_loop<false, true, NB>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   }
+  const float lt = half_sum(lsum);
+  if (!qvalid) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const size_t row = ((size_t)n * p.n_q + qrow) * p.n_q_heads + h;
+  if (p.out) {
+    bf16_t* op = p.out + row * D;
 #pragma unroll
-  for (int bl = 0; bl < NB; ++bl) {
-    const float lt = half_sum(lsum[bl]);
-    if (!qvalid[bl]) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const size_t row = ((size_t)n * p.n_q + qrow[bl]) * p.n_q_heads + h[bl];
-    if (p.out) {
-      bf16_t* op = p.out + row * D;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = a * 32 + 8 * i4 + 4 * g2;
-          const f32x16& oa = o[bl][a];
-          u32x2 w;
-          w[0] = (uint32_t)f32_to_bf16(oa[4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(oa[4 * i4 + 1] * inv) << 16);
-          w[1] = (uint32_t)f32_to_bf16(oa[4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(oa[4 * i4 + 3] * inv) << 16);
-          *(u32x2*)(op + d) = w;
-        }
-    }
-    if (p.lse && g2 == 0) p.lse[row] = lt > 0.f ? (m[bl] + log2f(lt)) * kLn2 : -INFINITY;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = a * 32 + 8 * i4 + 4 * g2;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[a][4 * i4 + 0] * inv, o[a][4 * i4 + 1] * inv);
+        w[1] = pack_bf16x2(o[a][4 * i4 + 2] * inv, o[a][4 * i4 + 3] * inv);
+        *(u32x2*)(op + d) = w;
+      }
   }
+  if (p.lse && g2 == 0) p.lse[row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
@@ -1047,19 +1015,17 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   const bool wave_live = q1 > q0;
 
   // Q as the B operand of S^T = K Q^T (one row block per wave)
-  bf16x8 qf1[1][8];
-  bf16x8 (&qf)[8] = qf1[0];
+  bf16x8 qf[8];
   {
     const bf16_t* qp = p.q + (((size_t)n * p.n_q + (qvalid ? qrow : 0)) * p.n_q_heads + h) * D + g2 * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) qf[c] = qvalid ? as_bf16x8(ld16(qp + c * 16)) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
-  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): Q is in registers before the tile loads start
+  // no wait here: the Q loads overlap the first tile loads; the waits of
+  // either phase cover them (loads complete in order)
 
-  float m1[1] = {-INFINITY}, lsum1[1] = {0.f};
-  float &m = m1[0], &lsum = lsum1[0];
-  f32x16 o1[1][4];
-  f32x16 (&o)[4] = o1[0];
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) o[a] = f32x16{};
 
@@ -1149,7 +1115,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     src.nk = p.n_kv;
     src.excl = p.excl + (size_t)min(b, p.B - 1) * p.excl_words;
     __builtin_amdgcn_s_setprio(1);  // ahead of the private phase's waves on the CU
-    tile_loop<true>(smem, src, p.c2, qf1, wave_live, wave, lane, m1, lsum1, o1);
+    tile_loop<true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -1222,8 +1188,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d = a * 32 + 8 * i4 + 4 * g2;
       u32x2 w;
-      w[0] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 0] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 1] * inv) << 16);
-      w[1] = (uint32_t)f32_to_bf16(o[a][4 * i4 + 2] * inv) | ((uint32_t)f32_to_bf16(o[a][4 * i4 + 3] * inv) << 16);
+      w[0] = pack_bf16x2(o[a][4 * i4 + 0] * inv, o[a][4 * i4 + 1] * inv);
+      w[1] = pack_bf16x2(o[a][4 * i4 + 2] * inv, o[a][4 * i4 + 3] * inv);
       *(u32x2*)(op + d) = w;
     }
   if (p.lse && g2 == 0) p.lse[row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
