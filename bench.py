@@ -624,6 +624,10 @@ def main():
     if mapped_mfma:
         map_kernels = ("attn_rows_mfma",)   # packed query-head groups, single pass
         roof_kernel = "read-slot attention, one call for all layers (attn_rows_mfma, query-head groups packed)"
+    elif w.batch < 2:
+        # one request shares the affix with no other: the shared-affix call runs the single pass
+        map_kernels = ("attn_split_mfma",)
+        roof_kernel = "read-slot attention, one shared-affix call for all layers (single pass: attn_split_mfma)"
     else:
         map_kernels = ("shared_plan_kernel", "attn_shared_mfma")
         roof_kernel = "read-slot attention, one shared-affix call for all layers (" + " + ".join(map_kernels) + ")"
