@@ -715,44 +715,42 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     }
     lsum += ls;
   };
-  // P.V of a weighed tile: P rounded to bf16 as the A operand's partner
-  auto absorb = [&](const bf16x8 (*pw)[2], int tile) {
-    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        // V^T operand: key slots follow the score tile's C layout (keys
-        // 4*g + 0..3 and 8 + 4*g + 0..3 of the 16-key block), two transposing
-        // reads
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pw[sub][hh], o[a]);
-        }
-      }
-  };
-  // Instruction order of the iteration body (the compiler keeps each LDS
-  // read next to the MFMA that takes it, so every MFMA would wait out a whole
-  // LDS latency): the score MFMAs of tile t+1, each K fragment read four
-  // MFMA groups ahead; then the P.V MFMAs of tile t, each group with its two
-  // transposing V reads four groups ahead and a share of tile t+1's scale
-  // products, exponentials, sums and bf16 conversions.
-  auto pipeline_body = [&]() {
-    constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+  // The matrix work of an iteration: the scores of tile t+1 (K fragments,
+  // accumulated from zero) and P.V of tile t (V^T fragments from transposing
+  // reads, P rounded to bf16 as the other operand), one MFMA of each in
+  // turn, so that the K and the V reads are spread evenly over the MFMAs.
+  // The V^T operand's key slots follow the score tile's C layout (keys
+  // 4*g + 0..3 and 8 + 4*g + 0..3 of each 16-key block).
+  auto score_absorb = [&](f32x16* s, int stile, const bf16x8 (*pw)[2], int vtile) {
+    const char* st = smem + (stile & 1) * KSTAGE;
+    const char* vst = smem + (2 + (vtile & 1)) * KSTAGE;
+    s[0] = s[1] = f32x16{};
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(2);  // see scores()
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);  // K reads, then the first V reads
+      const int c = i >> 1, sub = i & 1;
+      s[sub] = mfma(as_bf16x8(*(const u32x4*)(st + krd[c] + sub * 32 * ROWB)), qf[c], s[sub]);
+      const int vsub = i >> 3, hh = (i >> 2) & 1, a = i & 3;
+      const char* vp = vst + vrd[a] + (vsub * 32 + 16 * hh) * ROWB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+      o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pw[vsub][hh], o[a]);
     }
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
+  };
+  // Instruction order of that block (the compiler keeps each LDS read next
+  // to the MFMA that takes it, so every MFMA would wait out a whole LDS
+  // latency): reads two MFMA pairs ahead, the V pair after each score MFMA
+  // and the K fragment after each P.V MFMA.  The tile's weights follow.
+  auto pipeline = [&]() {
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       if (i < 14) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kValu, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
     }
   };
   // one iteration: pc holds the bf16 weights of tile t, pn receives those of
@@ -777,11 +775,10 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     if (!live) return;
     // past the last tile the scores read a stale stage and are never used;
     // computing them keeps the body branch-free
-    scores(sn, tile + 1);
-    absorb(pc, tile);
+    score_absorb(sn, tile + 1, pc, tile);
+    pipeline();
     float ls;
     weigh_fast(sn, pn, ls, f0, f1);
-    pipeline_body();
     if (tile + 1 < ntiles) weigh_check(sn, pn, tile + 1, ls, f0, f1);
   };
 
