@@ -1203,7 +1203,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
 // exponentials of tile t, it computes the scores of tile t+1.  Each score
 // accumulator starts at -LSE/scale of its row, so that the weight is
 // exp2(c2 * accumulator); those values come prepared by colmass_lse_prep
-// (padded with -inf to whole tiles) and reach LDS by direct loads too.
+// (padded with -inf to whole tiles) and reach LDS by direct loads too.  The
+// kernel fits three workgroups (three waves per SIMD) on a CU.
 __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
   __shared__ __attribute__((aligned(1024))) char Qs[2][32 * ROWB];
   __shared__ __attribute__((aligned(16))) float lse2[2][32];
@@ -1304,12 +1305,9 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     f32x16 init;
 #pragma unroll
     for (int i = 0; i < 16; ++i) init[i] = lse2[st][8 * (i >> 2) + 4 * g2 + (i & 3)];
-    // all eight Q fragments read before the first product, so the LDS
-    // reads overlap one another instead of each waiting for its MFMA pair
     bf16x8 qv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) qv[c] = as_bf16x8(*(const u32x4*)(qs + qrd[c]));
-    __builtin_amdgcn_sched_barrier(0);
     s[0] = init;
     s[1] = init;
 #pragma unroll
@@ -1354,6 +1352,22 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     for (int i = 0; i < 16; ++i) {
       acc0 += fast_exp2(sc[0][i] * p.c2);
       acc1 += fast_exp2(sc[1][i] * p.c2);
+    }
+    // Instruction order: the accumulator starts and three Q fragments read
+    // ahead, then each MFMA pair (one fragment, both key tiles) with the next
+    // fragment read and a share of tile t0's exponentials and sums, so that
+    // the LDS reads spread over the tile instead of arriving in one burst
+    {
+      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 7, 0);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        if (c < 5) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+      }
     }
     if (t1.b != t0.b) {  // last tile of this request: write its partial column masses
       const float a0 = half_sum(acc0);
