@@ -1030,9 +1030,11 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   const char* vbase = (const char*)p.pool_v + (size_t)layer * p.layer_bytes;
   const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
   const uint32_t head_off = (uint32_t)g * p.geo.page_size * ROWB;
+  // byte offset of a slot's row from the head's first row (page index and
+  // page bytes are below 2^24, the layer below 2^32: checked at launch)
+  const uint32_t row_mask = (uint32_t)(p.geo.page_size - 1) << 8;
   auto slot_off = [&](int32_t slot) -> uint32_t {
-    return ((uint32_t)slot >> p.geo.page_shift) * page_bytes + head_off +
-           ((uint32_t)slot & (uint32_t)(p.geo.page_size - 1)) * ROWB;
+    return __umul24((uint32_t)slot >> p.geo.page_shift, page_bytes) + (((uint32_t)slot << 8) & row_mask);
   };
   // DMA instruction i moves rows 4i + lane/16 (of a 16- or 32-row block),
   // one 16-byte chunk per lane; the global chunk is the swizzle of the LDS one
@@ -1132,17 +1134,20 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
 #pragma unroll
       for (int i = 0; i < PTILE; ++i) ps[i] = ptab[kb + i];
     };
+    // a tile's K loads record its row offsets, which its V loads reuse
+    const char* kbase_s = uniform_ptr(kbase + head_off);
+    const char* vbase_s = uniform_ptr(vbase + head_off);
+    uint32_t po[PTILE / 4];
     auto dma_k = [&]() {
 #pragma unroll
-      for (int i = 0; i < PTILE / 4; ++i)
-        dma16(kbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + kchunk[i & 3],
-              kdst + 4 * i * ROWB);
+      for (int i = 0; i < PTILE / 4; ++i) {
+        po[i] = slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3]));
+        dma16s(kbase_s, po[i] + kchunk[i & 3], kdst + 4 * i * ROWB);
+      }
     };
     auto dma_v = [&]() {
 #pragma unroll
-      for (int i = 0; i < PTILE / 4; ++i)
-        dma16(vbase + slot_off(pick(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3])) + vchunk,
-              vdst + 4 * i * ROWB);
+      for (int i = 0; i < PTILE / 4; ++i) dma16s(vbase_s, po[i] + vchunk, vdst + 4 * i * ROWB);
     };
     pload(0);
     dma_k();
@@ -1436,6 +1441,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   p.n_kv = a.n_kv;
   p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
   if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
+  // tile row offsets are 24-bit products of page index and page bytes
+  if ((size_t)a.geo.n_kv_heads * a.geo.page_size * D * 2 >= (1u << 24)) return hipErrorInvalidValue;
   p.B = B;
   p.n_q_heads = a.n_q_heads;
   p.layer_begin = a.layer_begin;
@@ -1481,6 +1488,8 @@ hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool d
   p.n_src = a.n_src;
   p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
   if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
+  // tile row offsets are 24-bit products of page index and page bytes
+  if ((size_t)a.geo.n_kv_heads * a.geo.page_size * D * 2 >= (1u << 24)) return hipErrorInvalidValue;
   // byte offsets of source rows within a layer are 32-bit in the tile loads
   if ((size_t)a.n_src * a.geo.n_kv_heads * D * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   p.B = a.B;
@@ -1513,6 +1522,8 @@ hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st, bool
   p.n_kv = a.L;
   p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
   if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
+  // tile row offsets are 24-bit products of page index and page bytes
+  if ((size_t)a.geo.n_kv_heads * a.geo.page_size * D * 2 >= (1u << 24)) return hipErrorInvalidValue;
   p.B = a.B;
   p.n_q_heads = a.n_q_heads;
   p.layer_begin = a.layer_begin;

@@ -36,6 +36,10 @@
  *  - head_dim is 16, 32, 64 or 128; page_size is a power of two <= 256;
  *    n_q_heads is a multiple of n_kv_heads and query head h reads KV head
  *    h / (n_q_heads / n_kv_heads).
+ *  - Size limits of the bf16 head_dim-128 kernels (ESHAPE, before anything
+ *    is enqueued): one layer of the pool below 4 GiB, and one page of one
+ *    layer (n_kv_heads * page_size rows of 256 bytes) below 16 MiB, since
+ *    row offsets are 32-bit byte offsets formed with 24-bit products.
  */
 #ifndef ACACHE_H
 #define ACACHE_H

@@ -221,6 +221,17 @@ def test_size_limits_rejected_before_any_launch():
     assert lib.acache_store_attend(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 8, 8, FAKE, FAKE,
                                    100, 1, 8, 0, 2, 0.1, FAKE, None, FAKE * 16, 1 << 24, None) == -3
     assert lib.acache_probe_attention(ctypes.byref(big), FAKE, 10, FAKE, 32, 8, 0, 2, 0.1, None, FAKE, None) == -3
+    # one page of one layer at 16 MiB (256 KV heads x 256 slots x 256 B): the 24-bit row-offset products overflow
+    wide = pool(n_pages=4, page_size=256, n_kv_heads=256)
+    assert lib.acache_mapped_attention(ctypes.byref(wide), FAKE, FAKE, 8, 8, FAKE, FAKE, 100, 1, 256, 0, 2, 0.1, FAKE,
+                                       None, None, 0, None) == -3
+    assert lib.acache_mapped_attention_shared_workspace_bytes(ctypes.byref(wide), 2, 16, 8, 256, 2, 100, 64,
+                                                              ctypes.byref(ws)) == 0
+    assert lib.acache_mapped_attention_shared(ctypes.byref(wide), FAKE, FAKE, 16, 8, FAKE, FAKE, 100, FAKE, 0, 64, 2,
+                                              256, 0, 2, 0.1, FAKE, None, FAKE * 16, max(ws.value, 16), None) == -3
+    assert lib.acache_store_attend(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 8, 8, FAKE, FAKE,
+                                   100, 1, 256, 0, 2, 0.1, FAKE, None, FAKE * 16, 1 << 24, None) == -3
+    assert lib.acache_probe_attention(ctypes.byref(wide), FAKE, 10, FAKE, 32, 256, 0, 2, 0.1, None, FAKE, None) == -3
 
 
 def _ws_query(lib, pl, B, n_q, mq, hq, nl, mkv, L):
