@@ -367,13 +367,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_mfma(AttnP p) {
 // Many-query attention (probe forward over the shared affix; read-slot
 // attention of recompute-sized query sets).  A workgroup owns 128 query rows
 // (32 per wave) and walks the key list in tiles of 64.  K and V tiles are
-// gathered through the slot table straight into a 2-stage LDS ring by
-// direct-to-LDS loads (no register staging); rows are stored as they sit in
-// the pool with their 16-byte chunks XOR-swizzled by row, and the V^T operands
-// of P.V come from transposing LDS reads.  Slot numbers arrive through scalar
-// loads a tile ahead, so the vector-memory counter tracks only tile loads; the
-// next tile's loads are in flight while the current one is computed, with one
-// barrier per tile.
+// gathered through the slot table straight into LDS (two K and two V
+// stages) by direct-to-LDS loads (no register staging); rows are stored as
+// they sit in the pool with their 16-byte chunks XOR-swizzled by row, and the
+// V^T operands of P.V come from transposing LDS reads.  Slot numbers arrive
+// through buffer loads a tile ahead; the next tile's loads are in flight while
+// the current one is computed, with one barrier per tile.
 namespace {
 constexpr int RB = 64;                   // keys per tile
 constexpr int RSTAGES = 2;
