@@ -571,6 +571,27 @@ int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const voi
 
 }  // extern "C"
 
+namespace {
+// workspace of the fused store-then-attend path (256-byte aligned parts)
+struct StoreWs {
+  bool fused = false;
+  int stride = 0;
+  size_t other = 0, counts = 0, total = 0;
+};
+
+StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, int32_t max_kv) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  StoreWs w;
+  w.fused = mfma_supported(pool->dtype, pool->head_dim) && max_q > 0 && max_kv <= kStorePlanMaxKv;
+  if (!w.fused) return w;
+  w.stride = max_kv;
+  w.other = 0;
+  w.counts = up((size_t)B * w.stride * 4);
+  w.total = w.counts + up((size_t)B * 4);
+  return w;
+}
+}  // namespace
+
 extern "C" {
 
 int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t max_q_per_req,
@@ -579,7 +600,7 @@ int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, i
   if (!bytes) return ACACHE_EINVAL;
   if ((st = check_pool(pool))) return st;
   if (B < 0 || max_q_per_req < 0 || max_kv_per_req < 0) return ACACHE_EINVAL;
-  *bytes = 0;  // the call needs none
+  *bytes = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req).total;
   return ACACHE_OK;
 }
 
@@ -589,10 +610,6 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
                         const int32_t* kv_offsets, int32_t max_kv_per_req, int32_t B, int32_t n_q_heads,
                         int32_t layer_begin, int32_t n_layers, float scale, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, acache_stream_t stream) {
-  (void)src_pos;
-  (void)src_offsets;
-  (void)workspace;
-  (void)workspace_bytes;
   int st;
   if ((st = check_pool(pool))) return st;
   if ((st = check_layers(pool, layer_begin, n_layers))) return st;
@@ -601,17 +618,59 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
     return ACACHE_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ACACHE_EINVAL;
   if (B > 65535) return ACACHE_ESHAPE;
-  if (n_src > 0 && (!k_src || !v_src || !src_slot)) return ACACHE_EINVAL;
+  if (n_src > 0 && (!k_src || !v_src || !src_pos || !src_slot || !src_offsets)) return ACACHE_EINVAL;
   if (n_src > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
-  // the definition itself: the scatter, then the attention through read_slot
-  // (the attention's arguments are checked before the scatter is enqueued)
+  const StoreWs w = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req);
+  // With more than three query heads per KV head the rows to store are few
+  // beside the attention, and splitting each key list in two costs a partial
+  // tile per unit: there the two calls measured faster than one.
+  const bool fused = w.fused && n_q_heads <= 3 * pool->n_kv_heads;
+  if (!fused || B == 0 || n_q == 0 || n_layers == 0) {
+    // the definition itself: the scatter, then the attention through
+    // read_slot (the attention's arguments are checked before the scatter)
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                    n_q_heads, layer_begin, n_layers, scale, out, lse, s, true)))
+      return st;
+    if ((st = acache_scatter_private(pool, k_src, v_src, src_slot, n_src, layer_begin, n_layers, stream))) return st;
+    return mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
+                                 n_q_heads, layer_begin, n_layers, scale, out, lse, s, false);
+  }
+  if (!q || !q_offsets || !kv_offsets || !out || !src_offsets) return ACACHE_EINVAL;
+  if (max_kv_per_req > 0 && !read_slot) return ACACHE_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return ACACHE_EALIGN;
+  if (!workspace || workspace_bytes < w.total) return ACACHE_EWORKSPACE;
+  if (!aligned16(workspace)) return ACACHE_EALIGN;
+  char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
-                                  n_q_heads, layer_begin, n_layers, scale, out, lse, s, true)))
-    return st;
-  if ((st = acache_scatter_private(pool, k_src, v_src, src_slot, n_src, layer_begin, n_layers, stream))) return st;
-  return mapped_attention_impl(pool, q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req, B,
-                               n_q_heads, layer_begin, n_layers, scale, out, lse, s, false);
+  StoreAttnArgs a;
+  a.q = q;
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.geo = geom_of(pool);
+  a.q_offsets = q_offsets;
+  a.n_q = n_q;
+  a.max_q = max_q_per_req;
+  a.other_slots = (const int32_t*)(ws + w.other);
+  a.other_counts = (const int32_t*)(ws + w.counts);
+  a.other_stride = w.stride;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.src_slot = src_slot;
+  a.src_offsets = src_offsets;
+  a.n_src = n_src;
+  a.B = B;
+  a.n_q_heads = n_q_heads;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  if ((st = limits_of(launch_attn_mfma_store(a, s, true)))) return st;
+  hipError_t e = launch_store_plan(read_slot, kv_offsets, src_pos, src_offsets, B, max_kv_per_req, w.stride,
+                                   (int32_t*)(ws + w.other), (int32_t*)(ws + w.counts), s);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(launch_attn_mfma_store(a, s));
 }
 
 int acache_hkvd_scores(const acache_kv_pool* pool, const int32_t* shared_slots, int32_t L, const void* k_full,

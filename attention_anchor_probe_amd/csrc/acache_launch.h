@@ -102,6 +102,15 @@ hipError_t launch_shared_plan(const int32_t* read_slot, const int32_t* kv_offset
                               int32_t* priv_counts, uint32_t* excl, int excl_words, hipStream_t st);
 constexpr int kSharedPrivTile = 32;  // private-list tile of attn_shared_mfma
 
+// Store-then-attend plan: per request, the read list without the positions
+// that the call stores (src_pos of src_offsets[b] .. src_offsets[b+1]), in
+// position order, into other_slots[b * stride ..], its length into
+// other_counts[b].  max_kv <= kStorePlanMaxKv (the position bitmap of one
+// request lives in LDS); stride >= max_kv.
+constexpr int kStorePlanMaxKv = 1 << 18;
+hipError_t launch_store_plan(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* src_pos,
+                             const int32_t* src_offsets, int B, int max_kv, int stride, int32_t* other_slots,
+                             int32_t* other_counts, hipStream_t st);
 // Checked mode: the pre-pass over a slot table (k_check.hip).  rec[0..2]
 // receive the smallest failing entry of ERANGE, EREGION and EDUP (INT32_MAX:
 // none); first is n_slots int32 of scratch in write mode.
@@ -145,6 +154,36 @@ inline int gqa_pack(int n_q_heads, int n_kv_heads, int max_q) {
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run = false);
 hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st, bool dry_run = false);
 
+// Store-then-attend, many-query MFMA path: request b's rows attend to
+// other_slots[b * other_stride .. + other_counts[b]) (pool slots) and to rows
+// src_offsets[b] .. src_offsets[b+1] of k_src / v_src
+// ([n_layers][n_src][n_kv_heads][128]), which are also copied to pool slots
+// src_slot[i] of the same layers.
+struct StoreAttnArgs {
+  const void* q;
+  void* pool_k;
+  void* pool_v;
+  PoolGeom geo;
+  const int32_t* q_offsets;
+  int n_q;
+  int max_q;
+  const int32_t* other_slots;
+  const int32_t* other_counts;
+  int other_stride;
+  const void* k_src;
+  const void* v_src;
+  const int32_t* src_slot;
+  const int32_t* src_offsets;
+  int n_src;
+  int B;
+  int n_q_heads;
+  int layer_begin;
+  int n_layers;
+  float scale;
+  void* out;
+  float* lse;
+};
+hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool dry_run = false);
 hipError_t launch_colmass_mfma(const ColmassArgs& a, hipStream_t st, bool dry_run = false);
 
 }  // namespace acache

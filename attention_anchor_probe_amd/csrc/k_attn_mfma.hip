@@ -8,6 +8,9 @@
 //     attn_rows_mfma   a workgroup owns 128 query rows (32 per wave) and every
 //                      wave walks every key (probe, recompute-sized sets;
 //                      grouped query heads packed into the rows of a unit);
+//     attn_store_rows_mfma  the same over a request's other keys and then its
+//                      freshly recomputed rows, read from their source while
+//                      the same launch stores them (store-then-attend);
 //     attn_split_mfma  a workgroup owns 32 query rows and its four waves split
 //                      each 128-key tile into four 32-key slices; the partial
 //                      (max, sum, O) of the waves are merged at the end
@@ -73,6 +76,17 @@ struct AttnP {
   const int32_t* priv_table;
   const int32_t* kv_counts;
   int kv_stride;
+  // attn_store_rows_mfma only: request b's fresh K/V rows are rows
+  // src_offsets[b] .. src_offsets[b+1] of src_k / src_v
+  // ([layers][n_src][n_kv_heads][128]); they are attended after its other keys
+  // (priv_table / kv_counts / kv_stride) and copied to pool slots src_slot[i]
+  const char* src_k;
+  const char* src_v;
+  const int32_t* src_slot;
+  const int32_t* src_offsets;
+  int n_src;
+  char* pool_kw;  // the pool, written by the copy
+  char* pool_vw;
   // attn_rows_mfma only: gpack > 1 packs the query heads of a KV-head group
   // into the rows of a unit (a unit is then a (layer, KV head, request, row
   // tile); its rows are the pairs (head g*gpack + j, query i), j-major), so
@@ -439,7 +453,9 @@ __device__ __forceinline__ uint32_t vswz2(uint32_t row, uint32_t chunk) { return
 }  // namespace
 
 // Key-list source of tile_loop: key j of the list is slot table[j] of the
-// (layer, KV head) whose rows start at kbase / vbase.
+// (layer, KV head) whose rows start at kbase / vbase.  A contiguous source
+// (tile_loop<_, true>) has no table: key j is row j, at byte offset
+// j * page_bytes from kbase / vbase (page_shift and page_mask 0).
 struct TileSrc {
   const char* kbase;
   const char* vbase;
@@ -457,7 +473,7 @@ struct TileSrc {
 // accumulators o) of this wave's 32 query rows, whose Q fragments are qf.
 // Every wave of the workgroup calls it: the tile loads are shared, and
 // waves with live == false only help load.
-template <bool EXCL>
+template <bool EXCL, bool CONTIG = false>
 __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[8],
                                           bool live, int wave, int lane, float& m, float& lsum, f32x16 (&o)[4]) {
   const int nk = src.nk;
@@ -482,11 +498,15 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // loads is one of the list's rows (finite; its weight is zero).
   const int32_t* vtable = src.table;
   const __amdgpu_buffer_rsrc_t trs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, nk * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, CONTIG ? 0 : nk * 4, 0x00020000);
   const uint32_t trow = (uint32_t)(16 * wave + sel) * 4;
   int32_t vs[4];
   auto sload = [&](int tile) {
-    if (tile * RB + RB <= nk) {
+    if constexpr (CONTIG) {
+      const int r0 = tile * RB + 16 * wave + sel;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vs[i] = min(r0 + 4 * i, nk - 1);
+    } else if (tile * RB + RB <= nk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, tile * (RB * 4) + 16 * i, 0);
     } else {
@@ -790,9 +810,15 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   }
 }
 
-// Many-query attention (attn_rows_mfma): a workgroup owns 128 query rows (32
-// per wave) of one (layer, head or packed head group, request) and walks the
-// whole key list with tile_loop.
+// Many-query attention (attn_rows_mfma and attn_store_rows_mfma): a
+// workgroup owns 128 query rows (32 per wave) of one (layer, head or packed
+// head group, request) and walks the whole key list with tile_loop.  STORE:
+// the key list is the request's other keys (priv_table) followed by its fresh
+// rows (src_k / src_v), and the units of one query head per KV head copy
+// those rows of their (layer, KV head) to the pool, a slice per row tile; the
+// call reads no slot it writes, so the copy needs no ordering against the
+// attention.
+template <bool STORE>
 __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
@@ -808,9 +834,45 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   const int g = packed ? hu : hu / (p.n_q_heads / p.geo.n_kv_heads);
   const int layer = p.layer_begin + n;
   const int tid = threadIdx.x, lane = tid & 63;
+  if constexpr (STORE) {
+    // the q_tiles units of one query head per KV head copy the rows of their
+    // (layer, KV head, request) to the pool, one slice each, 16 bytes a
+    // thread and four rows' loads in flight before their stores
+    if (packed || hu % (p.n_q_heads / p.geo.n_kv_heads) == 0) {
+      const int s0 = p.src_offsets[b], s1 = p.src_offsets[b + 1];
+      const int per = (s1 - s0 + p.q_tiles - 1) / p.q_tiles;
+      const int c0 = s0 + t * per, c1 = min(s1, c0 + per);
+      const size_t row_stride = (size_t)p.geo.n_kv_heads * ROWB;
+      const size_t sbase = (size_t)n * p.n_src * row_stride + (size_t)g * ROWB;
+      const size_t dbase = (size_t)layer * p.layer_bytes + (size_t)g * p.geo.page_size * ROWB;
+      const size_t page_bytes = (size_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+      const int c = tid & 15;
+      for (int i0 = c0 + (tid >> 4); i0 < c1; i0 += 4 * 16) {
+        u32x4 kx[4], vx[4];
+        size_t dof[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = min(i0 + 16 * u, c1 - 1);  // rows past c1 repeat the last row's copy
+          const uint32_t slot = (uint32_t)p.src_slot[i];
+          const size_t so = sbase + (size_t)i * row_stride + c * 16;
+          dof[u] = dbase + (size_t)(slot >> p.geo.page_shift) * page_bytes +
+                   (size_t)(slot & (p.geo.page_size - 1)) * ROWB + c * 16;
+          kx[u] = __builtin_nontemporal_load((const u32x4*)(p.src_k + so));
+          vx[u] = __builtin_nontemporal_load((const u32x4*)(p.src_v + so));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_nontemporal_store(kx[u], (u32x4*)(p.pool_kw + dof[u]));
+          __builtin_nontemporal_store(vx[u], (u32x4*)(p.pool_vw + dof[u]));
+        }
+      }
+    }
+  }
   int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
   if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
-  if (p.kv_offsets) {
+  if constexpr (STORE) {
+    k1 = p.kv_counts[b];
+  } else if (p.kv_offsets) {
     k0 = p.kv_offsets[b];
     k1 = p.kv_offsets[b + 1];
   }
@@ -858,10 +920,29 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   src.head_off = (uint32_t)g * p.geo.page_size * ROWB;
   src.page_shift = p.geo.page_shift;
   src.page_mask = (uint32_t)(p.geo.page_size - 1);
-  src.table = p.kv_table + k0;
+  src.table = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
   src.nk = nk;
   src.excl = nullptr;
   tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+  if constexpr (STORE) {
+    // the request's fresh rows, read from the source (rows s0 .. s1 of this
+    // layer and KV head, one row stride apart)
+    const int s0 = p.src_offsets[b], s1 = p.src_offsets[b + 1];
+    const size_t row_stride = (size_t)p.geo.n_kv_heads * ROWB;
+    const size_t off = ((size_t)n * p.n_src + s0) * row_stride + (size_t)g * ROWB;
+    TileSrc fresh;
+    fresh.kbase = p.src_k + off;
+    fresh.vbase = p.src_v + off;
+    fresh.page_bytes = (uint32_t)row_stride;
+    fresh.head_off = 0;
+    fresh.page_shift = 0;
+    fresh.page_mask = 0;
+    fresh.table = nullptr;
+    fresh.nk = s1 - s0;
+    fresh.excl = nullptr;
+    wg_barrier();  // every wave is done with the stages of the first list
+    tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+  }
   const float lt = half_sum(lsum);
   if (!qvalid) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -884,7 +965,12 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
 
 __global__ __launch_bounds__(256, 2) void attn_rows_mfma(AttnP p) {
   __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
-  rows_body(p, smem);
+  rows_body<false>(p, smem);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_store_rows_mfma(AttnP p) {
+  __shared__ __attribute__((aligned(1024))) char smem[RSTAGES * RSTAGE_BYTES];
+  rows_body<true>(p, smem);
 }
 
 // Read-slot attention of decode blocks whose requests share one affix
@@ -1374,7 +1460,52 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   return hipGetLastError();
 }
 
-
+hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool dry_run) {
+  const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
+  if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
+  const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
+  AttnP p{};
+  p.q = (const bf16_t*)a.q;
+  p.pool_k = (const bf16_t*)a.pool_k;
+  p.pool_v = (const bf16_t*)a.pool_v;
+  p.pool_kw = (char*)a.pool_k;
+  p.pool_vw = (char*)a.pool_v;
+  p.geo = a.geo;
+  p.q_offsets = a.q_offsets;
+  p.n_q = a.n_q;
+  const long long q_tiles = (rows + 127) / 128;
+  if (q_tiles > (1ll << 30)) return hipErrorInvalidValue;
+  p.q_tiles = (int)q_tiles;
+  p.gpack = G;
+  p.priv_table = a.other_slots;
+  p.kv_counts = a.other_counts;
+  p.kv_stride = a.other_stride;
+  p.src_k = (const char*)a.k_src;
+  p.src_v = (const char*)a.v_src;
+  p.src_slot = a.src_slot;
+  p.src_offsets = a.src_offsets;
+  p.n_src = a.n_src;
+  p.layer_bytes = (size_t)a.geo.n_pages * a.geo.n_kv_heads * a.geo.page_size * D * 2;
+  if (p.layer_bytes >= (1ull << 32)) return hipErrorInvalidValue;
+  // tile row offsets are 24-bit products of page index and page bytes
+  if ((size_t)a.geo.n_kv_heads * a.geo.page_size * D * 2 >= (1u << 24)) return hipErrorInvalidValue;
+  // byte offsets of source rows within a layer are 32-bit in the tile loads
+  if ((size_t)a.n_src * a.geo.n_kv_heads * D * 2 >= (1ull << 32)) return hipErrorInvalidValue;
+  p.B = a.B;
+  p.n_q_heads = a.n_q_heads;
+  p.layer_begin = a.layer_begin;
+  p.c2 = a.scale * kLog2e;
+  p.out = (bf16_t*)a.out;
+  p.lse = a.lse;
+  const long long units = (long long)a.n_layers * (G > 0 ? a.geo.n_kv_heads : a.n_q_heads) * a.B * q_tiles;
+  if (units == 0) return hipSuccess;
+  if (units > (1ll << 30)) return hipErrorInvalidValue;
+  p.n_units = (int)units;
+  p.per_xcd = (int)((units + 7) / 8);
+  if (dry_run) return hipSuccess;
+  hipLaunchKernelGGL(attn_store_rows_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_mfma_shared(const SharedAttnArgs& a, hipStream_t st, bool dry_run) {
   if (a.max_q > 32) return hipErrorInvalidValue;

@@ -3,8 +3,8 @@
 //     Diffusion Large Language Models", Section 3.2),
 //   * the write-side recomputation map and the per-request read-slot map
 //     (Section 4.1 dual mapping, Section 4.2 admission-time preparation),
-//   * the plan of the shared-affix attention (each request's read list split
-//     by where its keys are read from),
+//   * the plans of the shared-affix and store-then-attend attentions (each
+//     request's read list split by where its keys are read from),
 //   * decode-block destination slots (Section 4.3, block decoding),
 //   * the private scatter of recomputed K/V rows (Section 4.3 and
 //     Appendix C.1: new KV is stored through the write-side map before the
@@ -265,6 +265,56 @@ hipError_t launch_shared_plan(const int32_t* read_slot, const int32_t* kv_offset
   if (pad < 1 || pad > kTopkThreads || stride < (max_kv + pad - 1) / pad * pad) return hipErrorInvalidValue;
   hipLaunchKernelGGL(shared_plan_kernel, dim3(B), dim3(kTopkThreads), 0, st, read_slot, kv_offsets, shared_slots,
                      affix_l, L, max_kv, stride, pad, priv_slots, priv_counts, excl, excl_words);
+  return hipGetLastError();
+}
+
+// Store-then-attend plan (Section 4.3: the recomputed rows are stored to
+// their private slots and read back by the attention).  Per request b, the
+// read list without the positions this call stores: positions src_pos[i]
+// (i in src_offsets[b] .. src_offsets[b+1]) are marked in an LDS bitmap and
+// every other position p < T_b contributes read_slot[kv_offsets[b] + p], in
+// position order, to other_slots[b * stride ..]; other_counts[b] receives
+// the count.  Positions past max_kv are ignored.
+__global__ __launch_bounds__(kTopkThreads) void store_plan_kernel(
+    const int32_t* __restrict__ read_slot, const int32_t* __restrict__ kv_offsets,
+    const int32_t* __restrict__ src_pos, const int32_t* __restrict__ src_offsets, int max_kv, int stride,
+    int32_t* __restrict__ other_slots, int32_t* __restrict__ other_counts) {
+  extern __shared__ uint32_t marked[];  // (max_kv + 31) / 32 words
+  __shared__ uint32_t wave_tot[kTopkWaves + 1];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int k0 = kv_offsets[b];
+  const int T = min(kv_offsets[b + 1] - k0, max_kv);
+  const int words = (T + 31) / 32;
+  for (int w = tid; w < words; w += kTopkThreads) marked[w] = 0u;
+  __syncthreads();
+  for (int i = src_offsets[b] + tid; i < src_offsets[b + 1]; i += kTopkThreads) {
+    const int pos = src_pos[i];
+    if (pos >= 0 && pos < T) atomicOr(&marked[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  const int32_t* rs = read_slot + k0;
+  int32_t* out = other_slots + (size_t)b * stride;
+  uint32_t base = 0;
+  for (int p0 = 0; p0 < T; p0 += kTopkThreads) {
+    const int pos = p0 + tid;
+    const bool keep = pos < T && !((marked[pos >> 5] >> (pos & 31)) & 1u);
+    const int32_t slot = keep ? rs[pos] : 0;
+    uint32_t tot;
+    const uint32_t at = block_exclusive_scan(keep ? 1u : 0u, wave_tot, &tot);
+    if (keep) out[base + at] = slot;
+    base += tot;
+  }
+  if (tid == 0) other_counts[b] = (int32_t)base;
+}
+
+hipError_t launch_store_plan(const int32_t* read_slot, const int32_t* kv_offsets, const int32_t* src_pos,
+                             const int32_t* src_offsets, int B, int max_kv, int stride, int32_t* other_slots,
+                             int32_t* other_counts, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  if (max_kv < 0 || max_kv > kStorePlanMaxKv || stride < max_kv) return hipErrorInvalidValue;
+  const size_t lds = (size_t)((max_kv + 31) / 32) * 4;
+  hipLaunchKernelGGL(store_plan_kernel, dim3(B), dim3(kTopkThreads), lds, st, read_slot, kv_offsets, src_pos,
+                     src_offsets, max_kv, stride, other_slots, other_counts);
   return hipGetLastError();
 }
 

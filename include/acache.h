@@ -348,13 +348,26 @@ int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const voi
  *               position src_pos[i] of its request, to be stored at src_slot[i].
  *  q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req,
  *  out, lse    as for acache_mapped_attention.
- * The call runs exactly that: the scatter, then the attention (all
- * arguments are checked before the scatter is enqueued).  src_pos and
- * src_offsets say which position of which request each row holds; the
- * result does not depend on them and they may be NULL.  The workspace
- * arguments are unused (the size query returns 0) and may be NULL / 0.
- * Errors as for the two calls.  Nothing is enqueued when an error is
- * returned.
+ * For bf16 pools with head_dim 128 and at most three query heads per KV head,
+ * one plan kernel and one attention kernel run: each request's rows attend to
+ * its read list without its src_pos
+ * positions (read from the pool) and to its source rows (read from k_src /
+ * v_src), while one unit per (layer, KV head, request) copies the source rows
+ * to src_slot.  That equals the definition when, as the maps of
+ * acache_build_maps arrange for the recompute set, each src_slot[i] is read at
+ * position src_pos[i] of request b (read_slot[kv_offsets[b] + src_pos[i]] ==
+ * src_slot[i]) and at no other position of any request; keys are then summed
+ * in another order (fp32 rounding only).  Other pools, more query heads per
+ * KV head (few rows to store beside the attention, where the two calls are
+ * faster), or calls without query rows, run the two calls of the definition
+ * and leave the workspace unused.
+ * Workspace: size from acache_store_attend_workspace_bytes (given the same
+ * pool, B, max_q_per_req and max_kv_per_req; about 4 * B * max_kv_per_req
+ * bytes, or 0 when no call with that pool can take the one-kernel path),
+ * 16-byte aligned, rewritten by every call (calls sharing it must not
+ * overlap).  max_kv_per_req <= 262144 on the one-kernel path.
+ * Errors as for the two calls; EWORKSPACE when the workspace is missing or
+ * small.  Nothing is enqueued when an error is returned.
  */
 int acache_store_attend_workspace_bytes(const acache_kv_pool* pool, int32_t B, int32_t max_q_per_req,
                                         int32_t max_kv_per_req, size_t* bytes /*host*/);

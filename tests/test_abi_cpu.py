@@ -173,30 +173,35 @@ def test_shared_attention_validation_and_workspace():
 
 
 def test_store_attend_validation_and_workspace():
-    """The store-then-attend call runs its definition (the scatter, then the
-    read-slot attention) and needs no workspace; every argument is checked
-    before anything is enqueued."""
     lib = Bd._lib()
     p = pool()
 
     def ws(pl, B=3, mq=100, mkv=500):
-        out = ctypes.c_size_t(123)
+        out = ctypes.c_size_t()
         assert lib.acache_store_attend_workspace_bytes(ctypes.byref(pl), B, mq, mkv, ctypes.byref(out)) == 0
         return out.value
-    assert ws(p) == 0 and ws(p, mkv=1 << 20) == 0 and ws(pool(dtype=0, head_dim=64)) == 0
+    need = ws(p)
+    assert need >= 3 * 500 * 4 + 3 * 4          # other read lists and their counts
+    assert ws(p, mkv=1000) > need
+    assert ws(p, mq=0) == 0                       # no query rows: the scatter alone
+    assert ws(pool(dtype=0, head_dim=64)) == 0    # other pools: the two calls of the definition
+    assert ws(p, mkv=(1 << 18) + 1) == 0          # longer contexts: the two calls
     sa = lambda **kw: lib.acache_store_attend(
-        ctypes.byref(kw.pop("pool", p)), kw.get("ks", FAKE), kw.get("vs", FAKE), FAKE, kw.get("sl", FAKE), FAKE,
+        ctypes.byref(kw.pop("pool", p)), kw.get("ks", FAKE), kw.get("vs", FAKE), FAKE, FAKE, kw.get("so", FAKE),
         kw.get("ns", 10), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE, kw.get("mkv", 100),
-        kw.get("B", 1), kw.get("hq", 4), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, None, 0, None)
+        kw.get("B", 1), kw.get("hq", 4), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None,
+        kw.get("ws", FAKE * 16), kw.get("wsb", 1 << 24), None)
     assert sa(B=0, ns=0) == 0
     assert sa(hq=5) == -3
     assert sa(mq=9) == -1 and sa(ns=-1) == -1
     assert sa(scale=-1.0) == -1
     assert sa(B=70000) == -3
-    assert sa(ks=None) == -1 and sa(sl=None) == -1
+    assert sa(ks=None) == -1 and sa(so=None) == -1
     assert sa(ks=FAKE_MIS) == -9
     assert sa(out=None) == -1
     assert sa(q=FAKE_MIS) == -9
+    assert sa(wsb=16) == -7 and sa(ws=None) == -7
+    assert sa(ws=FAKE + 4) == -9
 
 
 def test_size_limits_rejected_before_any_launch():

@@ -373,7 +373,7 @@ def test_gqa_decode_attention_packed(hq, hkv):
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 4, 4), ("bf16", 128, 6, 2), ("bf16", 128, 8, 2),
                                              ("f32", 32, 4, 2)],
-                         ids=["bf16-mha", "bf16-gqa3", "bf16-gqa4", "f32"])
+                         ids=["bf16-mha", "bf16-gqa3-packed", "bf16-gqa4-two-calls", "f32-two-calls"])
 def test_store_attend_seeded(dtype, d, hq, hkv):
     """Store-then-attend of the recompute phase (Section 4.3): the pool after
     the call equals the oracle's scatter byte for byte, and the attention
