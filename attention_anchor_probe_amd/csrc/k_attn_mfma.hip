@@ -8,9 +8,10 @@
 //     attn_rows_mfma   a workgroup owns 128 query rows (32 per wave) and every
 //                      wave walks every key (probe, recompute-sized sets;
 //                      grouped query heads packed into the rows of a unit);
-//     attn_store_rows_mfma  the same over a request's other keys and then its
-//                      freshly recomputed rows, read from their source while
-//                      the same launch stores them (store-then-attend);
+//     attn_store_rows_mfma  the same over a request's freshly recomputed
+//                      rows, read from their source while the same launch
+//                      stores them, and then its other keys
+//                      (store-then-attend);
 //     attn_split_mfma  a workgroup owns 32 query rows and its four waves split
 //                      each 128-key tile into four 32-key slices; the partial
 //                      (max, sum, O) of the waves are merged at the end
@@ -78,7 +79,7 @@ struct AttnP {
   int kv_stride;
   // attn_store_rows_mfma only: request b's fresh K/V rows are rows
   // src_offsets[b] .. src_offsets[b+1] of src_k / src_v
-  // ([layers][n_src][n_kv_heads][128]); they are attended after its other keys
+  // ([layers][n_src][n_kv_heads][128]); they are attended before its other keys
   // (priv_table / kv_counts / kv_stride) and copied to pool slots src_slot[i]
   const char* src_k;
   const char* src_v;
@@ -813,8 +814,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
 // Many-query attention (attn_rows_mfma and attn_store_rows_mfma): a
 // workgroup owns 128 query rows (32 per wave) of one (layer, head or packed
 // head group, request) and walks the whole key list with tile_loop.  STORE:
-// the key list is the request's other keys (priv_table) followed by its fresh
-// rows (src_k / src_v), and the units of one query head per KV head copy
+// the key list is the request's fresh rows (src_k / src_v) followed by its
+// other keys (priv_table), and the units of one query head per KV head copy
 // those rows of their (layer, KV head) to the pool, a slice per row tile; the
 // call reads no slot it writes, so the copy needs no ordering against the
 // attention.
@@ -923,10 +924,13 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   src.table = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
   src.nk = nk;
   src.excl = nullptr;
-  tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
-  if constexpr (STORE) {
-    // the request's fresh rows, read from the source (rows s0 .. s1 of this
-    // layer and KV head, one row stride apart)
+  if constexpr (!STORE) {
+    tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+  } else {
+    // the request's fresh rows first, read from the source (rows s0 .. s1 of
+    // this layer and KV head, one row stride apart): they hold the anchors,
+    // the keys of largest attention mass, so the running max is near its
+    // final value before the other keys come and the exact step is rare
     const int s0 = p.src_offsets[b], s1 = p.src_offsets[b + 1];
     const size_t row_stride = (size_t)p.geo.n_kv_heads * ROWB;
     const size_t off = ((size_t)n * p.n_src + s0) * row_stride + (size_t)g * ROWB;
@@ -940,8 +944,9 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
     fresh.table = nullptr;
     fresh.nk = s1 - s0;
     fresh.excl = nullptr;
-    wg_barrier();  // every wave is done with the stages of the first list
     tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    wg_barrier();  // every wave is done with the stages of the first list
+    tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   }
   const float lt = half_sum(lsum);
   if (!qvalid) return;

@@ -350,10 +350,9 @@ int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const voi
  *  out, lse    as for acache_mapped_attention.
  * For bf16 pools with head_dim 128 and at most three query heads per KV head,
  * one plan kernel and one attention kernel run: each request's rows attend to
- * its read list without its src_pos
- * positions (read from the pool) and to its source rows (read from k_src /
- * v_src), while one unit per (layer, KV head, request) copies the source rows
- * to src_slot.  That equals the definition when, as the maps of
+ * its source rows (read from k_src / v_src) and then to its read list without
+ * its src_pos positions (read from the pool), while one unit per (layer, KV
+ * head, request) copies the source rows to src_slot.  That equals the definition when, as the maps of
  * acache_build_maps arrange for the recompute set, each src_slot[i] is read at
  * position src_pos[i] of request b (read_slot[kv_offsets[b] + src_pos[i]] ==
  * src_slot[i]) and at no other position of any request; keys are then summed
