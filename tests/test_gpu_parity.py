@@ -381,7 +381,21 @@ def test_store_attend_seeded(dtype, d, hq, hkv):
     the oracle on seeded anchors.  Request 1 stores nothing (its recompute
     positions keep the pool's old rows), request 2 has no query rows (its rows
     must still be stored), request 0 has many query rows over several tiles."""
-    w = Workload(104, "sa", dtype, 2, hq, hkv, d, (("req", 24), ("affix", 300), ("req", 9), ("gen", 64)), 4, 0.2,
+    _store_attend_case(dtype, d, hq, hkv, 0.2)
+
+
+@pytest.mark.parametrize("rate", [0.0, 1.0], ids=["no-anchors", "every-affix-position"])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2)], ids=["mha", "gqa3-packed"])
+def test_store_attend_anchor_rates(hq, hkv, rate):
+    """The same at the ratio extremes (Section 4.3 with ratio 0 and 1): with
+    no anchors only the request's own positions are stored; with every affix
+    position an anchor the storing requests read nothing but their fresh rows,
+    so the second key list of the one-kernel path is empty."""
+    _store_attend_case("bf16", 128, hq, hkv, rate)
+
+
+def _store_attend_case(dtype, d, hq, hkv, rate):
+    w = Workload(104, "sa", dtype, 2, hq, hkv, d, (("req", 24), ("affix", 300), ("req", 9), ("gen", 64)), 4, rate,
                  page_order="random")
     K = A.acache_anchor_count(w.L, w.rate)
     lay = gen.make_layout(w, K, 9)
