@@ -670,8 +670,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     return expsum(s, m == -INFINITY ? 0.f : -m);
   };
   // Weights of a freshly scored tile against the running max as it stands
-  // (weigh_fast, in the iteration body, also past the last tile, where the
-  // weights are never used) and their check (weigh_check).  When every
+  // (weigh_fast, in the iteration body) and their check (weigh_check).  When every
   // lane's sum stays at most 2^8 (so every weight does, as with a running max
   // within 8 of the true one), the weights are kept; otherwise (a key above
   // the running max by more than a factor 8 on average, or no finite running
@@ -773,13 +772,28 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     }
     if (tile + 1 < ntiles) dma_v(tile + 1, oc);
     if (!live) return;
-    // past the last tile the scores read a stale stage and are never used;
-    // computing them keeps the body branch-free
     score_absorb(sn, tile + 1, pc, tile);
     pipeline();
     float ls;
     weigh_fast(sn, pn, ls, f0, f1);
-    if (tile + 1 < ntiles) weigh_check(sn, pn, tile + 1, ls, f0, f1);
+    weigh_check(sn, pn, tile + 1, ls, f0, f1);
+  };
+
+  // the last iteration: P.V of the last tile only (there is no next tile to
+  // score, so its body is the absorb half of score_absorb)
+  auto last_step = [&](int tile, const bf16x8 (*pc)[2]) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): V(t) has landed
+    wg_barrier();                        // ... in every wave
+    if (!live) return;
+    const char* vst = smem + (2 + (tile & 1)) * KSTAGE;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int vsub = i >> 3, hh = (i >> 2) & 1, a = i & 3;
+      const char* vp = vst + vrd[a] + (vsub * 32 + 16 * hh) * ROWB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+      o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pc[vsub][hh], o[a]);
+    }
   };
 
   bf16x8 pa[2][2], pb[2][2];
@@ -805,9 +819,13 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       to_bf16(sn, pa);
     }
   }
-  for (int tile = 0; tile < ntiles; tile += 2) {
+  for (int tile = 0; tile < ntiles - 1; tile += 2) {
     step(tile, pa, pb, oa, ob, xa, xb);
-    if (tile + 1 < ntiles) step(tile + 1, pb, pa, ob, oa, xb, xa);
+    if (tile + 2 < ntiles) step(tile + 1, pb, pa, ob, oa, xb, xa);
+  }
+  if (ntiles > 0) {
+    if (ntiles & 1) last_step(ntiles - 1, pa);
+    else last_step(ntiles - 1, pb);
   }
 }
 
