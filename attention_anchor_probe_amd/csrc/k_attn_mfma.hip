@@ -454,9 +454,10 @@ __device__ __forceinline__ uint32_t vswz2(uint32_t row, uint32_t chunk) { return
 }  // namespace
 
 // Key-list source of tile_loop: key j of the list is slot table[j] of the
-// (layer, KV head) whose rows start at kbase / vbase.  A contiguous source
-// (tile_loop<_, true>) has no table: key j is row j, at byte offset
-// j * page_bytes from kbase / vbase (page_shift and page_mask 0).
+// (layer, KV head) whose rows start at kbase / vbase.  A mixed source
+// (tile_loop<_, true>) puts nf rows of a contiguous buffer first: keys
+// 0 .. nf-1 are rows 0 .. nf-1 at byte offset j * fstride from fkbase /
+// fvbase, and keys nf .. nk-1 are slots table[0 .. nk-nf-1].
 struct TileSrc {
   const char* kbase;
   const char* vbase;
@@ -467,6 +468,10 @@ struct TileSrc {
   const int32_t* table;
   int nk;
   const uint32_t* excl;  // EXCL only: bit j of excl[j / 32] set drops key j (padded to 64-key tiles)
+  const char* fkbase;    // MIXED only
+  const char* fvbase;
+  uint32_t fstride;
+  int nf;
 };
 
 // Streams a key list through the workgroup's LDS in 64-key tiles into the
@@ -474,7 +479,7 @@ struct TileSrc {
 // accumulators o) of this wave's 32 query rows, whose Q fragments are qf.
 // Every wave of the workgroup calls it: the tile loads are shared, and
 // waves with live == false only help load.
-template <bool EXCL, bool CONTIG = false>
+template <bool EXCL, bool MIXED = false>
 __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float c2, const bf16x8 (&qf)[8],
                                           bool live, int wave, int lane, float& m, float& lsum, f32x16 (&o)[4]) {
   const int nk = src.nk;
@@ -496,17 +501,34 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // Full tiles read their four slots through a buffer resource (lane part
   // in the vector offset, tile and row-group parts in the scalar offset).  The last, partial tile clamps
   // its rows to the last key of the list instead, so that every V row it
-  // loads is one of the list's rows (finite; its weight is zero).
+  // loads is one of the list's rows (finite; its weight is zero).  MIXED:
+  // key j below nf is row j of the contiguous buffer; the others read
+  // table[j - nf] through a buffer resource sized to the table (the loads of
+  // keys below nf read its first entry and are not used).
+  const int nf = MIXED ? src.nf : 0;
   const int32_t* vtable = src.table;
   const __amdgpu_buffer_rsrc_t trs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, CONTIG ? 0 : nk * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, (nk - nf) * 4, 0x00020000);
   const uint32_t trow = (uint32_t)(16 * wave + sel) * 4;
   int32_t vs[4];
+  // the list position of the row this lane moves in DMA instruction i
+  auto key_of = [&](int tile, int i) { return min(tile * RB + 16 * wave + sel + 4 * i, nk - 1); };
   auto sload = [&](int tile) {
-    if constexpr (CONTIG) {
-      const int r0 = tile * RB + 16 * wave + sel;
+    if constexpr (MIXED) {
+      // contiguous rows need no table read; whole table tiles read it as
+      // below, shifted by nf; the tile across nf and the last partial tile
+      // read it per lane.  A loaded value is used a tile later (selecting
+      // between it and the row index here would wait for the load)
+      if (tile * RB + RB <= nf) {
+      } else if (tile * RB >= nf && tile * RB + RB <= nk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vs[i] = min(r0 + 4 * i, nk - 1);
+        for (int i = 0; i < 4; ++i)
+          vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, (tile * RB - nf) * 4 + 16 * i, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, (uint32_t)max(key_of(tile, i) - nf, 0) * 4, 0, 0);
+      }
     } else if (tile * RB + RB <= nk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, tile * (RB * 4) + 16 * i, 0);
@@ -529,24 +551,66 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   const char* kbase_s = uniform_ptr(src.kbase + src.head_off);
   const char* vbase_s = uniform_ptr(src.vbase + src.head_off);
   const uint32_t rmask = src.page_mask << 8;
+  const char* fkbase_s = MIXED ? uniform_ptr(src.fkbase) : nullptr;
+  const char* fvbase_s = MIXED ? uniform_ptr(src.fvbase) : nullptr;
   // K loads of a tile also record its row offsets (off, with the K chunk),
-  // which its V loads reuse one iteration later
+  // which its V loads reuse one iteration later.  MIXED: a lane whose key
+  // is below nf loads from the contiguous buffer; only the tile across nf
+  // has lanes of both kinds
+  auto pool_off = [&](int i) {
+    const uint32_t slot = (uint32_t)vs[i];
+    // page index and page bytes are below 2^24, their product plus the row
+    // offset below 2^32; the row part (bits 8..) and the chunk part (bits
+    // 4..7) do not overlap
+    return __umul24(slot >> src.page_shift, src.page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
+  };
+  // row bytes and row count below 2^24, their product below 2^32; a whole
+  // tile of contiguous rows splits the offset into a tile part (scalar) and
+  // this lane's row and chunk
+  auto fresh_off = [&](int tile, int i) { return __umul24((uint32_t)key_of(tile, i), src.fstride) + kchunk[i]; };
+  const uint32_t frow0 = MIXED ? __umul24((uint32_t)(16 * wave + sel), src.fstride) : 0u;
+  auto fresh_off_full = [&](int tile, int i) {
+    return __umul24((uint32_t)(tile * RB + 4 * i), src.fstride) + frow0 + kchunk[i];
+  };
   auto dma_k = [&](int tile, uint32_t* off) {
     const uint32_t st = lds0 + (tile & 1) * KSTAGE;
+    if (!MIXED || tile * RB >= nf) {  // only table keys (uniform)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t slot = (uint32_t)vs[i];
-      // page index and page bytes are below 2^24, their product plus the
-      // row offset below 2^32; the row part (bits 8..) and the chunk part
-      // (bits 4..7) do not overlap
-      off[i] = __umul24(slot >> src.page_shift, src.page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
-      dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      for (int i = 0; i < 4; ++i) {
+        off[i] = pool_off(i);
+        dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      }
+    } else if (tile * RB + RB <= nf) {  // only contiguous rows (uniform)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        off[i] = fresh_off_full(tile, i);
+        dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+      }
+    } else {  // the one tile across nf: per lane
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool fr = key_of(tile, i) < nf;
+        off[i] = fr ? fresh_off(tile, i) : pool_off(i);
+        if (fr) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+        else dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      }
     }
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
+    if (!MIXED || tile * RB >= nf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+      for (int i = 0; i < 4; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    } else if (tile * RB + RB <= nf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16s(fvbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (key_of(tile, i) < nf) dma16s(fvbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+        else dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+      }
+    }
   };
 
   // per-lane LDS read offsets within a stage (row and swizzle parts; the tile
@@ -945,26 +1009,20 @@ __device__ __forceinline__ void rows_body(const AttnP& p, char* smem) {
   if constexpr (!STORE) {
     tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   } else {
-    // the request's fresh rows first, read from the source (rows s0 .. s1 of
-    // this layer and KV head, one row stride apart): they hold the anchors,
-    // the keys of largest attention mass, so the running max is near its
-    // final value before the other keys come and the exact step is rare
+    // one list: the request's fresh rows first, read from the source (rows
+    // s0 .. s1 of this layer and KV head, one row stride apart), then its
+    // other keys.  The fresh rows hold the anchors, the keys of largest
+    // attention mass, so the running max is near its final value before
+    // the other keys come and the exact step is rare
     const int s0 = p.src_offsets[b], s1 = p.src_offsets[b + 1];
     const size_t row_stride = (size_t)p.geo.n_kv_heads * ROWB;
     const size_t off = ((size_t)n * p.n_src + s0) * row_stride + (size_t)g * ROWB;
-    TileSrc fresh;
-    fresh.kbase = p.src_k + off;
-    fresh.vbase = p.src_v + off;
-    fresh.page_bytes = (uint32_t)row_stride;
-    fresh.head_off = 0;
-    fresh.page_shift = 0;
-    fresh.page_mask = 0;
-    fresh.table = nullptr;
-    fresh.nk = s1 - s0;
-    fresh.excl = nullptr;
-    tile_loop<false, true>(smem, fresh, p.c2, qf, wave_live, wave, lane, m, lsum, o);
-    wg_barrier();  // every wave is done with the stages of the first list
-    tile_loop<false>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
+    src.fkbase = p.src_k + off;
+    src.fvbase = p.src_v + off;
+    src.fstride = (uint32_t)row_stride;
+    src.nf = s1 - s0;
+    src.nk = src.nf + nk;
+    tile_loop<false, true>(smem, src, p.c2, qf, wave_live, wave, lane, m, lsum, o);
   }
   const float lt = half_sum(lsum);
   if (!qvalid) return;
