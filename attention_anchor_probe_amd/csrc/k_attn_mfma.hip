@@ -799,7 +799,6 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
       o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pw[vsub][hh], o[a]);
     }
-    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
   };
   // Instruction order of that block (the compiler keeps each LDS read next
   // to the MFMA that takes it, so every MFMA would wait out a whole LDS
@@ -838,6 +837,10 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
     if (!live) return;
     score_absorb(sn, tile + 1, pc, tile);
     pipeline();
+    // back to the phase's priority only after the scheduling groups: an
+    // s_setprio bounds a scheduling region, and one inside the block would
+    // leave its MFMAs and LDS reads outside the groups
+    if constexpr (EXCL) __builtin_amdgcn_s_setprio(1);
     float ls;
     weigh_fast(sn, pn, ls, f0, f1);
     weigh_check(sn, pn, tile + 1, ls, f0, f1);
@@ -1116,70 +1119,6 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
   auto slot_off = [&](int32_t slot) -> uint32_t {
     return __umul24((uint32_t)slot >> p.geo.page_shift, page_bytes) + (((uint32_t)slot << 8) & row_mask);
   };
-  // DMA instruction i moves rows 4i + lane/16 (of a 16- or 32-row block),
-  // one 16-byte chunk per lane; the global chunk is the swizzle of the LDS one
-  const int sel = lane >> 4;
-  uint32_t kchunk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane & 15) * 16;
-  const uint32_t vchunk = vswz2(sel, lane & 15) * 16;
-  auto pick = [&](int32_t s0, int32_t s1, int32_t s2, int32_t s3) {
-    return (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
-  };
-  uint32_t krd[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) krd[c] = l32 * ROWB + kswz(l32, 2 * c + g2) * 16;
-  const uint32_t i16 = lane & 15;
-  uint32_t vrd[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const uint32_t row = 4 * g2 + (i16 >> 2);
-    const uint32_t dcol = a * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-    vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
-  }
-
-  // online-softmax update with NS 32-key score blocks (C layout) and the
-  // P.V product with V^T read from the V rows at vst
-  auto update = [&](auto ns, f32x16* s, const char* vst) {
-    constexpr int NS = decltype(ns)::value;
-    float mr = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < NS; ++sub)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
-    mr = half_max(mr);
-    const float mt = mr * p.c2;
-    if (mt > m + 8.f) {  // lazy rescale, exact either way
-      const float alpha = exp2f(m - mt);
-      lsum *= alpha;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
-      m = mt;
-    }
-    const float nm = (m == -INFINITY) ? 0.f : -m;
-#pragma unroll
-    for (int sub = 0; sub < NS; ++sub)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
-          lsum += pv;
-          pb[j] = (__bf16)pv;
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-          o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
-        }
-      }
-  };
-
   // ---- shared phase: the affix keys, loaded once for the four requests
   auto shared_phase = [&]() {
     if (p.n_kv <= 0) return;
@@ -1203,6 +1142,80 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma(AttnP p) {
     if (!wave_live) return;
     const int cnt = ((sc_i32)p.kv_counts)[b];
     if (cnt <= 0) return;
+    // every load issued before this phase (the Q rows among them) is waited
+    // for here, at no cost after the shared phase's own final wait; without
+    // it the compiler waits for them inside the loop, where the wait would
+    // also drain the tile's V loads
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    // per-lane constants of this phase, computed here from a lane index the
+    // compiler cannot trace back, so that none of them is held in registers
+    // through the shared phase
+    int lane_p;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_p) : "v"(lane));
+    // DMA instruction i moves rows 4i + lane/16 (of a 16- or 32-row block),
+    // one 16-byte chunk per lane; the global chunk is the swizzle of the LDS one
+    const int sel = lane_p >> 4;
+    uint32_t kchunk[4];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) kchunk[i] = kswz(4 * i + sel, lane_p & 15) * 16;
+    const uint32_t vchunk = vswz2(sel, lane_p & 15) * 16;
+    auto pick = [&](int32_t s0, int32_t s1, int32_t s2, int32_t s3) {
+      return (sel & 2) ? ((sel & 1) ? s3 : s2) : ((sel & 1) ? s1 : s0);
+    };
+    uint32_t krd[8];
+  #pragma unroll
+    for (int c = 0; c < 8; ++c) krd[c] = (lane_p & 31) * ROWB + kswz(lane_p & 31, 2 * c + (lane_p >> 5)) * 16;
+    const uint32_t i16 = lane_p & 15;
+    uint32_t vrd[4];
+  #pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint32_t row = 4 * (lane_p >> 5) + (i16 >> 2);
+      const uint32_t dcol = a * 32 + 16 * ((lane_p >> 4) & 1) + 4 * (i16 & 3);
+      vrd[a] = row * ROWB + vswz2(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+    }
+
+    // online-softmax update with NS 32-key score blocks (C layout) and the
+    // P.V product with V^T read from the V rows at vst
+    auto update = [&](auto ns, f32x16* s, const char* vst) {
+      constexpr int NS = decltype(ns)::value;
+      float mr = -INFINITY;
+  #pragma unroll
+      for (int sub = 0; sub < NS; ++sub)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) mr = fmaxf(mr, s[sub][i]);
+      mr = half_max(mr);
+      const float mt = mr * p.c2;
+      if (mt > m + 8.f) {  // lazy rescale, exact either way
+        const float alpha = exp2f(m - mt);
+        lsum *= alpha;
+  #pragma unroll
+        for (int a = 0; a < 4; ++a)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) o[a][i] *= alpha;
+        m = mt;
+      }
+      const float nm = (m == -INFINITY) ? 0.f : -m;
+  #pragma unroll
+      for (int sub = 0; sub < NS; ++sub)
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 pb;
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float pv = fast_exp2(fmaf(s[sub][8 * hh + j], p.c2, nm));
+            lsum += pv;
+            pb[j] = (__bf16)pv;
+          }
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const char* vp = vst + vrd[a] + (sub * 32 + 16 * hh) * ROWB;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+            o[a] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[a]);
+          }
+        }
+    };
+
     sc_i32 ptab = (sc_i32)(p.priv_table + (size_t)b * p.kv_stride);
     const char* reg = smem + wave * (PTILE * ROWB * 2);  // K rows, then V rows
     const uint32_t kdst = lds_addr(reg), vdst = kdst + PTILE * ROWB;
