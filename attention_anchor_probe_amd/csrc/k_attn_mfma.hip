@@ -1443,6 +1443,10 @@ __global__ __launch_bounds__(256, 2) void colmass_mfma(ColP p) {
     }
     const It t4 = next(t3);
     in = rows_load(t3);
+    // keep those loads here, at the top of the iteration: the compiler
+    // would sink them to its end, where its wait for them at the loop edge
+    // would then stall
+    asm volatile("" ::: "memory");
     // past the last tile the scores read a stale stage and are never used;
     // computing them keeps this block branch-free
     scores(sn, st ^ 1);
