@@ -384,13 +384,18 @@ def test_store_attend_seeded(dtype, d, hq, hkv):
     _store_attend_case(dtype, d, hq, hkv, 0.2)
 
 
-@pytest.mark.parametrize("rate", [0.0, 1.0], ids=["no-anchors", "every-affix-position"])
+@pytest.mark.parametrize("rate", [0.0, 0.103, 0.105, 1.0],
+                         ids=["no-anchors", "fresh-rows-end-on-a-tile", "one-fresh-row-past-a-tile",
+                              "every-affix-position"])
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2)], ids=["mha", "gqa3-packed"])
 def test_store_attend_anchor_rates(hq, hkv, rate):
-    """The same at the ratio extremes (Section 4.3 with ratio 0 and 1): with
-    no anchors only the request's own positions are stored; with every affix
-    position an anchor the storing requests read nothing but their fresh rows,
-    so the second key list of the one-kernel path is empty."""
+    """The same at the ratio extremes (Section 4.3 with ratio 0 and 1) and
+    where the fresh rows meet the pool keys: with no anchors only the
+    request's own positions are stored; at ratio 0.103 a storing request has
+    128 fresh rows, two whole 64-key tiles, so no tile of the one-kernel path
+    mixes fresh rows and pool slots; at 0.105 it has 129, one row into the
+    next tile; with every affix position an anchor the storing requests read
+    nothing but their fresh rows."""
     _store_attend_case("bf16", 128, hq, hkv, rate)
 
 
