@@ -513,7 +513,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   int32_t vs[4];
   // the list position of the row this lane moves in DMA instruction i
   auto key_of = [&](int tile, int i) { return min(tile * RB + 16 * wave + sel + 4 * i, nk - 1); };
-  auto sload = [&](int tile) {
+  auto sload = [&](int tile, int32_t* vs) {
     if constexpr (MIXED) {
       // contiguous rows need no table read; whole table tiles read it as
       // below, shifted by nf; the tile across nf and the last partial tile
@@ -557,7 +557,7 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   // which its V loads reuse one iteration later.  MIXED: a lane whose key
   // is below nf loads from the contiguous buffer; only the tile across nf
   // has lanes of both kinds
-  auto pool_off = [&](int i) {
+  auto pool_off = [&](const int32_t* vs, int i) {
     const uint32_t slot = (uint32_t)vs[i];
     // page index and page bytes are below 2^24, their product plus the row
     // offset below 2^32; the row part (bits 8..) and the chunk part (bits
@@ -572,29 +572,38 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   auto fresh_off_full = [&](int tile, int i) {
     return __umul24((uint32_t)(tile * RB + 4 * i), src.fstride) + frow0 + kchunk[i];
   };
-  auto dma_k = [&](int tile, uint32_t* off) {
-    const uint32_t st = lds0 + (tile & 1) * KSTAGE;
+  // a K tile's row offsets from its slots (koff), then its loads (kissue)
+  auto koff = [&](int tile, uint32_t* off, const int32_t* vs) {
     if (!MIXED || tile * RB >= nf) {  // only table keys (uniform)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        off[i] = pool_off(i);
-        dma16s(kbase_s, off[i], st + 4 * i * ROWB);
-      }
+      for (int i = 0; i < 4; ++i) off[i] = pool_off(vs, i);
     } else if (tile * RB + RB <= nf) {  // only contiguous rows (uniform)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        off[i] = fresh_off_full(tile, i);
-        dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
-      }
+      for (int i = 0; i < 4; ++i) off[i] = fresh_off_full(tile, i);
     } else {  // the one tile across nf: per lane
 #pragma unroll
+      for (int i = 0; i < 4; ++i) off[i] = key_of(tile, i) < nf ? fresh_off(tile, i) : pool_off(vs, i);
+    }
+  };
+  auto kissue = [&](int tile, const uint32_t* off) {
+    const uint32_t st = lds0 + (tile & 1) * KSTAGE;
+    if (!MIXED || tile * RB >= nf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+    } else if (tile * RB + RB <= nf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+    } else {
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool fr = key_of(tile, i) < nf;
-        off[i] = fr ? fresh_off(tile, i) : pool_off(i);
-        if (fr) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+        if (key_of(tile, i) < nf) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
         else dma16s(kbase_s, off[i], st + 4 * i * ROWB);
       }
     }
+  };
+  auto dma_k = [&](int tile, uint32_t* off, const int32_t* vs) {
+    koff(tile, off, vs);
+    kissue(tile, off);
   };
   auto dma_v = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * KSTAGE;
@@ -830,8 +839,8 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
       xload(tile + 2, xn);
     }
     if (tile + 2 < ntiles) {
-      dma_k(tile + 2, on);
-      if (tile + 3 < ntiles) sload(tile + 3);
+      dma_k(tile + 2, on, vs);
+      if (tile + 3 < ntiles) sload(tile + 3, vs);
     }
     if (tile + 1 < ntiles) dma_v(tile + 1, oc);
     if (!live) return;
@@ -867,16 +876,21 @@ __device__ __forceinline__ void tile_loop(char* smem, const TileSrc& src, float 
   uint32_t oa[4], ob[4];
   uint32_t xa[2] = {0u, 0u}, xb[2] = {0u, 0u};
   if (ntiles > 0) {
-    sload(0);
-    dma_k(0, ob);
+    // the slots of tiles 0 and 1 in one round trip, both tiles' offsets
+    // (the one wait for them, before any tile load: the compiler does not
+    // count the tile loads, and a wait for a slot load issued before one of
+    // them would drain it too), then the loads of K0, V0 and K1
+    int32_t v1[4];
+    sload(0, vs);
+    if (ntiles > 1) sload(1, v1);
+    koff(0, ob, vs);
+    if (ntiles > 1) koff(1, oa, v1);
+    kissue(0, ob);
     dma_v(0, ob);
+    if (ntiles > 1) kissue(1, oa);
     xload(0, xb);
     xload(1, xa);
-    if (ntiles > 1) {
-      sload(1);
-      dma_k(1, oa);
-      if (ntiles > 2) sload(2);
-    }
+    if (ntiles > 2) sload(2, vs);
     __builtin_amdgcn_s_waitcnt(0x3F70);
     wg_barrier();
     if (live) {
