@@ -579,10 +579,21 @@ struct StoreWs {
   size_t other = 0, counts = 0, total = 0;
 };
 
+// Largest recompute set per request (query rows) that takes the one-kernel
+// path.  The kernel saves the scatter's pass over the rows, which grows with
+// the rows, but every row tile of a request reads the request's source rows
+// (256 bytes per KV head, a whole position's row apart) where the two calls
+// read runs of pool slots, a cost that grows with the rows times the row
+// tiles.  With one query head per KV head the one kernel measured 2% faster
+// at 1332 and 1536 rows per request, 0.4-0.6% slower at 1741 and 1-3.5% slower
+// from 2151 rows up (12 layers, 16 and 32 requests, alternated on one box).
+constexpr int32_t kStoreOneKernelMaxRows = 1536;
+
 StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, int32_t max_kv) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   StoreWs w;
-  w.fused = mfma_supported(pool->dtype, pool->head_dim) && max_q > 0 && max_kv <= kStorePlanMaxKv;
+  w.fused = mfma_supported(pool->dtype, pool->head_dim) && max_q > 0 && max_q <= kStoreOneKernelMaxRows &&
+            max_kv <= kStorePlanMaxKv;
   if (!w.fused) return w;
   w.stride = max_kv;
   w.other = 0;
@@ -621,10 +632,11 @@ int acache_store_attend(const acache_kv_pool* pool, const void* k_src, const voi
   if (n_src > 0 && (!k_src || !v_src || !src_pos || !src_slot || !src_offsets)) return ACACHE_EINVAL;
   if (n_src > 0 && (!aligned16(k_src) || !aligned16(v_src))) return ACACHE_EALIGN;
   const StoreWs w = store_ws_layout(pool, B, max_q_per_req, max_kv_per_req);
-  // With more than three query heads per KV head the rows to store are few
-  // beside the attention, and splitting each key list in two costs a partial
-  // tile per unit: there the two calls measured faster than one.
-  const bool fused = w.fused && n_q_heads <= 3 * pool->n_kv_heads;
+  // With grouped query heads the rows to store are fewer beside the
+  // attention: two query heads per KV head measured 0.7-1.9% slower in one
+  // kernel than in the two calls (1332-2970 rows per request), so only
+  // one query head per KV head takes the one kernel.
+  const bool fused = w.fused && n_q_heads == pool->n_kv_heads;
   if (!fused || B == 0 || n_q == 0 || n_layers == 0) {
     // the definition itself: the scatter, then the attention through
     // read_slot (the attention's arguments are checked before the scatter)

@@ -130,7 +130,7 @@ def test_scatter_and_attention_validation():
     assert sc(pool=pool(dtype=3)) == -2
     at = lambda **kw: lib.acache_mapped_attention(
         ctypes.byref(p), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE, 100,
-        kw.get("B", 1), kw.get("hq", 4), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, None, 0, None)
+        kw.get("B", 1), kw.get("hq", 2), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None, None, 0, None)
     assert at(B=0) == 0
     assert at(hq=5) == -3
     assert at(mq=9) == -1
@@ -186,10 +186,11 @@ def test_store_attend_validation_and_workspace():
     assert ws(p, mq=0) == 0                       # no query rows: the scatter alone
     assert ws(pool(dtype=0, head_dim=64)) == 0    # other pools: the two calls of the definition
     assert ws(p, mkv=(1 << 18) + 1) == 0          # longer contexts: the two calls
+    assert ws(p, mq=1536) > 0 and ws(p, mq=1537) == 0   # larger recompute sets: the two calls
     sa = lambda **kw: lib.acache_store_attend(
         ctypes.byref(kw.pop("pool", p)), kw.get("ks", FAKE), kw.get("vs", FAKE), FAKE, FAKE, kw.get("so", FAKE),
         kw.get("ns", 10), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE, kw.get("mkv", 100),
-        kw.get("B", 1), kw.get("hq", 4), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None,
+        kw.get("B", 1), kw.get("hq", 2), 0, 2, kw.get("scale", 0.1), kw.get("out", FAKE), None,
         kw.get("ws", FAKE * 16), kw.get("wsb", 1 << 24), None)
     assert sa(B=0, ns=0) == 0
     assert sa(hq=5) == -3
@@ -202,6 +203,10 @@ def test_store_attend_validation_and_workspace():
     assert sa(q=FAKE_MIS) == -9
     assert sa(wsb=16) == -7 and sa(ws=None) == -7
     assert sa(ws=FAKE + 4) == -9
+    # grouped query heads or more rows per request take the two calls, which
+    # need no workspace: the first launch fails instead (EDEVICE, no GPU here)
+    assert sa(hq=4, ws=None, wsb=0) == -8
+    assert sa(nq=1537, mq=1537, ws=None, wsb=0) == -8
 
 
 def test_size_limits_rejected_before_any_launch():

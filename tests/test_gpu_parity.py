@@ -373,7 +373,7 @@ def test_gqa_decode_attention_packed(hq, hkv):
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 4, 4), ("bf16", 128, 6, 2), ("bf16", 128, 8, 2),
                                              ("f32", 32, 4, 2)],
-                         ids=["bf16-mha", "bf16-gqa3-packed", "bf16-gqa4-two-calls", "f32-two-calls"])
+                         ids=["bf16-mha-one-kernel", "bf16-gqa3-two-calls", "bf16-gqa4-two-calls", "f32-two-calls"])
 def test_store_attend_seeded(dtype, d, hq, hkv):
     """Store-then-attend of the recompute phase (Section 4.3): the pool after
     the call equals the oracle's scatter byte for byte, and the attention
@@ -387,7 +387,7 @@ def test_store_attend_seeded(dtype, d, hq, hkv):
 @pytest.mark.parametrize("rate", [0.0, 0.103, 0.105, 1.0],
                          ids=["no-anchors", "fresh-rows-end-on-a-tile", "one-fresh-row-past-a-tile",
                               "every-affix-position"])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2)], ids=["mha", "gqa3-packed"])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 8)], ids=["mha4", "mha8"])
 def test_store_attend_anchor_rates(hq, hkv, rate):
     """The same at the ratio extremes (Section 4.3 with ratio 0 and 1) and
     where the fresh rows meet the pool keys: with no anchors only the
