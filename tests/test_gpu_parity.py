@@ -399,8 +399,18 @@ def test_store_attend_anchor_rates(hq, hkv, rate):
     _store_attend_case("bf16", 128, hq, hkv, rate)
 
 
-def _store_attend_case(dtype, d, hq, hkv, rate):
-    w = Workload(104, "sa", dtype, 2, hq, hkv, d, (("req", 24), ("affix", 300), ("req", 9), ("gen", 64)), 4, rate,
+@pytest.mark.parametrize("anchors", [1439, 1440], ids=["1536-rows-one-kernel", "1537-rows-two-calls"])
+def test_store_attend_row_limit(anchors):
+    """The one kernel takes at most 1536 query rows per request (max_q_per_req);
+    one row more and the call makes the two calls of its definition.  Both
+    sides of that limit store the rows byte for byte and attend as the
+    oracle: request 0 recomputes 97 own positions plus its anchors, all of
+    them query rows."""
+    _store_attend_case("bf16", 128, 4, 4, anchors / 1800, affix=1800, expect_rows=anchors + 97)
+
+
+def _store_attend_case(dtype, d, hq, hkv, rate, affix=300, expect_rows=None):
+    w = Workload(104, "sa", dtype, 2, hq, hkv, d, (("req", 24), ("affix", affix), ("req", 9), ("gen", 64)), 4, rate,
                  page_order="random")
     K = A.acache_anchor_count(w.L, w.rate)
     lay = gen.make_layout(w, K, 9)
@@ -426,6 +436,11 @@ def _store_attend_case(dtype, d, hq, hkv, rate):
     q = gen.make_rows(w, int(q_off[-1]), gen.S_QRC, device=DEV, heads=w.n_q_heads, seed=9)
     torch.cuda.synchronize()
     kh, vh, qh, skh, svh = np_of(k), np_of(v), np_of(q), np_of(src_k), np_of(src_v)
+    if expect_rows is not None:
+        assert max(q_counts) == expect_rows
+        one_kernel = A.acache_store_attend_workspace_bytes(k, v, B=w.batch, max_q_per_req=max(q_counts),
+                                                           max_kv_per_req=w.T) > 0
+        assert one_kernel == (expect_rows <= 1536)
     out = torch.full_like(q, 7.0)
     lse = torch.empty(q.shape[:3], device=DEV)
     A.acache_store_attend(k, v, src_k, src_v, i32(rc_pos), i32(rc_slot), i32(src_off), q, i32(q_off), i32(read),
