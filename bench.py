@@ -271,7 +271,8 @@ class Setup:
         of the same shape; timed on its own.  The full-prompt K/V of the first
         nb requests that fit in half of the free device memory are timed (all
         of them unless the workload is the L=16384 one) and the time scaled to
-        every request.  Returns (ms, algorithmic GB, nb)."""
+        every request.  Returns (ms, algorithmic GB, nb, the rate of the timed
+        calls over the bytes they read: nb requests' K/V and the affix once)."""
         w = self.w
         per_req = 2 * w.n_layers * w.L * w.n_kv_heads * w.head_dim * 2
         free, _ = torch.cuda.mem_get_info()
@@ -289,9 +290,14 @@ class Setup:
             ev[i + 1].record()
         torch.cuda.synchronize()
         # every request's full-prompt K/V once, and the shared affix K/V once
-        gb = (per_req * w.batch + 2 * w.L * w.n_layers * w.n_kv_heads * w.head_dim * 2) / 1e9
+        affix = 2 * w.L * w.n_layers * w.n_kv_heads * w.head_dim * 2
+        gb = (per_req * w.batch + affix) / 1e9
         del kf, vf, sc
-        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * w.batch / nb, gb, nb
+        t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        # a call on nb < B requests reads the affix once for nb requests, so
+        # the scaled time charges it B / nb times; the timed calls' own rate:
+        timed_gbs = (per_req * nb + affix) / 1e9 / (t * 1e-3)
+        return t * w.batch / nb, gb, nb, timed_gbs
 
     def probe_single_request(self, reps):
         """The probe of one request alone at the same shapes (its non-affix
@@ -578,7 +584,7 @@ def main():
         dropna_ms = S.dropna_ms(max(3, args.steps // 2))
         progress("single-pass, recompute, store-then-attend and DropNA timings done")
         fn_ms, fn_overlap, fn_one_ms = S.full_normaliser()
-        hk_ms, hk_gb, hk_nb = S.hkvd_ms(3)
+        hk_ms, hk_gb, hk_nb, hk_timed_gbs = S.hkvd_ms(3)
         progress("full-context normaliser and HKVD timings done")
         single_req = S.probe_single_request(max(3, args.steps // 2))
         cold_warm = S.mapped_cold_warm(max(5, args.steps))
@@ -598,7 +604,7 @@ def main():
                                 "one_pass_ms": fn_one_ms,
                                 "one_pass_extra_ms": fn_one_ms - stage_mean("probe_attention")},
             "hkvd_selector": {"ms": hk_ms, "algorithmic_gb": hk_gb, "gbs": hk_gb / (hk_ms * 1e-3),
-                              "requests_timed": hk_nb},
+                              "requests_timed": hk_nb, "timed_calls_gbs": hk_timed_gbs},
         }
     fp = A.acache_kv_footprint([w.T] * w.batch, w.L, S.K, w.page_size, w.n_layers, w.n_kv_heads, w.head_dim, w.dtype)
     stage_t = {name: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
