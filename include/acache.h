@@ -349,24 +349,24 @@ int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const voi
  *  q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req,
  *  out, lse    as for acache_mapped_attention.
  * For bf16 pools with head_dim 128, one query head per KV head and
- * max_q_per_req <= 1536, one plan kernel and one attention kernel run: each request's rows attend to
- * its source rows (read from k_src / v_src) and then to its read list without
- * its src_pos positions (read from the pool), while one unit per (layer, KV
- * head, request) copies the source rows to src_slot.  That equals the definition when, as the maps of
- * acache_build_maps arrange for the recompute set, each src_slot[i] is read at
- * position src_pos[i] of request b (read_slot[kv_offsets[b] + src_pos[i]] ==
- * src_slot[i]) and at no other position of any request; keys are then summed
- * in another order (fp32 rounding only).  Other pools, grouped query heads
- * (fewer rows to store beside the attention), more query rows per request
- * (each row tile reads every source row of its request), or calls without
- * query rows, run the two calls of the definition, which are faster there,
- * and leave the workspace unused.
+ * max_q_per_req <= 1536, one plan kernel and one attention kernel run: each
+ * request's rows attend to its source rows (read from k_src / v_src) and
+ * then to its read list without its src_pos positions (read from the pool),
+ * while the row tiles of each (layer, KV head, request) copy its source rows
+ * to src_slot, a slice each.  That equals the definition when, as the maps
+ * of acache_build_maps arrange for the recompute set, each src_slot[i] is
+ * read at position src_pos[i] of request b (read_slot[kv_offsets[b] +
+ * src_pos[i]] == src_slot[i]) and at no other position of any request; keys
+ * are then summed in another order (fp32 rounding only).  Other pools,
+ * grouped query heads (fewer rows to store beside the attention), more query
+ * rows per request (each row tile reads every source row of its request), or
+ * calls without query rows, run the two calls of the definition, which are
+ * faster there, and leave the workspace unused.
  * Workspace: size from acache_store_attend_workspace_bytes (given the same
  * pool, B, max_q_per_req and max_kv_per_req; about 4 * B * max_kv_per_req
  * bytes, or 0 when no call with that pool and max_q_per_req can take the
- * one-kernel path),
- * 16-byte aligned, rewritten by every call (calls sharing it must not
- * overlap).  max_kv_per_req <= 262144 on the one-kernel path.
+ * one-kernel path), 16-byte aligned, rewritten by every call (calls sharing
+ * it must not overlap).  max_kv_per_req <= 262144 on the one-kernel path.
  * Errors as for the two calls; EWORKSPACE when the workspace is missing or
  * small.  Nothing is enqueued when an error is returned.
  */
