@@ -580,14 +580,14 @@ struct StoreWs {
 };
 
 // Largest recompute set per request (query rows) that takes the one-kernel
-// path.  The kernel saves the scatter's pass over the rows, which grows with
-// the rows, but every row tile of a request reads the request's source rows
-// (256 bytes per KV head, a whole position's row apart) where the two calls
-// read runs of pool slots, a cost that grows with the rows times the row
-// tiles.  With one query head per KV head the one kernel measured 2% faster
-// at 1332 and 1536 rows per request, 0.4-0.6% slower at 1741 and 1-3.5% slower
-// from 2151 rows up (12 layers, 16 and 32 requests, alternated on one box).
-constexpr int32_t kStoreOneKernelMaxRows = 1536;
+// path, whose attention is the 32-row tile loop.  Against the two calls with
+// the same tile loop, the one kernel saves the scatter's pass over the rows
+// but reads every source row once per row tile of its request: it measured
+// 2% faster at 1332 and 1536 rows per request and slower from 1741 rows up
+// (one query head per KV head, 12 layers, alternated on one box).  From
+// kRows48MinRows rows up the two calls' attention is the 48-row kernel, and
+// the two calls are faster (46.3 against 48.9 ms at 1332 rows, L=4096).
+constexpr int32_t kStoreOneKernelMaxRows = (int32_t)kRows48MinRows - 1;
 
 StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, int32_t max_kv) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };

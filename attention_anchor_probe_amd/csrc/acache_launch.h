@@ -147,6 +147,11 @@ inline int gqa_pack(int n_q_heads, int n_kv_heads, int max_q) {
   const int G = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 1;
   return (G > 1 && (max_q > 32 || (long long)G * max_q >= 128)) ? G : 0;
 }
+// Units of at least this many query rows (after packing) take the many-query
+// kernel with 48 rows per wave on the 16x16x32 MFMA (192-row tiles); smaller
+// ones the 32-row tile loop (128-row tiles), where a 192-row tile would leave
+// too many waves without rows.
+constexpr long long kRows48MinRows = 384;
 // The MFMA launches check the sizes their kernels index with 32 bits;
 // dry_run = true checks them (same return value) and launches nothing, so
 // that a call made of several launches can reject its arguments before it

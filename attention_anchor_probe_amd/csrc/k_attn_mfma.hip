@@ -1071,6 +1071,373 @@ __global__ __launch_bounds__(256, 2) void attn_store_rows_mfma(AttnP p) {
   rows_body<true>(p, smem);
 }
 
+// Many-query attention on the 16x16x32 MFMA with 48 query rows per wave
+// (three 16-row blocks), 192 rows per workgroup (attn_rows48_mfma).  Every K
+// fragment read from LDS (16 keys x 32 dims) feeds the score MFMAs of the
+// three row blocks, and every V^T fragment (16 dims x 32 keys) their three
+// P.V MFMAs, so a 32-key tile takes two thirds of the LDS fragment reads and
+// two thirds of the tile loads per FLOP of the 32-row tile loop, at 2 waves
+// per SIMD.
+//
+// MFMA 16x16x32 operand mapping (lane l, r = l % 16, q = l / 16):
+//   A (16 x 32): lane holds row r, eight K-slots (q, j), j = 0..7
+//   B (32 x 16): lane holds column r, the same eight K-slots
+//   C (16 x 16): lane holds column r, rows 4*q + i, i = 0..3
+// Scores are computed transposed (S^T = K Q^T, head dim d = 32c + 8q + j for
+// MFMA step c), so a lane holds one query row and keys 16*kb + 4q + i of key
+// block kb; the P.V product takes those eight weights as its B operand, with
+// K-slot j meaning key 4q + j (j < 4) or 16 + 4q + j - 4 of the tile.
+namespace {
+constexpr int T48 = 32;                      // keys per tile
+constexpr uint32_t T48_BYTES = T48 * ROWB;   // one K or V tile: 8 KiB
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16-byte chunk swizzle of a V row in this kernel's tiles: a transposing
+// read of one 32-lane half covers rows 8h .. 8h+7 at two chunks each, which
+// this spreads over all 64 banks (the second read of a fragment, 16 rows on,
+// keeps the swizzle)
+__device__ __forceinline__ uint32_t vswz48(uint32_t row, uint32_t chunk) { return chunk ^ ((row & 7u) << 1); }
+// max / sum over the four lanes of a query row (l, l^16, l^32, l^48)
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
+  // two K stages then two V stages of 32-key tiles
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T48_BYTES];
+  const int unit = xcd_unit(p.per_xcd);
+  if (unit >= p.n_units) return;
+  const bool packed = p.gpack > 1;
+  const int n_uh = packed ? p.geo.n_kv_heads : p.n_q_heads;  // heads that index units
+  int r = unit;
+  const int t = r % p.q_tiles;
+  r /= p.q_tiles;
+  const int b = r % p.B;
+  r /= p.B;
+  const int hu = r % n_uh;
+  const int n = r / n_uh;
+  const int g = packed ? hu : hu / (p.n_q_heads / p.geo.n_kv_heads);
+  const int layer = p.layer_begin + n;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
+  if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
+  if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
+  const int nq = q1 - q0;
+  const int rows = packed ? p.gpack * nq : nq;
+  const int rbase = t * 192;
+  if (rbase >= rows) return;
+  const int nk = k1 - k0;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, qd = lane >> 4;
+  // this wave holds rows rbase + 48 * wave + 16 * rb + r16 (rb = 0..2)
+  const int wrow = rbase + 48 * wave;
+  const bool live = wrow < rows;
+  int qrow[3], qhead[3];
+  bool qvalid[3];
+  bf16x8 qf[3][4];
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    const int lrow = wrow + 16 * rb + r16;
+    qvalid[rb] = lrow < rows;
+    // lanes past the rows take the first row and head of the unit (loaded,
+    // never stored)
+    qrow[rb] = q0 + (qvalid[rb] ? lrow : 0);
+    qhead[rb] = hu;
+    if (packed) {
+      const int j = qvalid[rb] ? lrow / nq : 0;
+      qrow[rb] = q0 + (qvalid[rb] ? lrow - j * nq : 0);
+      qhead[rb] = g * p.gpack + j;
+    }
+    const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow[rb]) * p.n_q_heads + qhead[rb]) * D + 8 * qd;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qf[rb][c] = qvalid[rb] ? as_bf16x8(ld16(qp + 32 * c)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+
+  float m[3] = {-INFINITY, -INFINITY, -INFINITY}, lsum[3] = {0.f, 0.f, 0.f};
+  f32x4 o[8][3];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) o[db][rb] = f32x4{};
+
+  const float c2 = p.c2;
+  const int ntiles = (nk + T48 - 1) / T48;
+  // tile loads: this wave moves rows 8*wave .. 8*wave+7 of each K and V tile;
+  // DMA instruction i covers rows 8*wave + 4i + lane/16, one 16-byte chunk
+  // per lane
+  const int sel = lane >> 4;
+  const int32_t* vtable = p.kv_table + k0;
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, nk * 4, 0x00020000);
+  const uint32_t trow = (uint32_t)(8 * wave + sel) * 4;
+  auto sload = [&](int tile, int32_t* vs) {
+    if (tile * T48 + T48 <= nk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, tile * (T48 * 4) + 16 * i, 0);
+    } else {
+      // the last partial tile repeats the list's last key (finite rows;
+      // their scores are masked)
+      const int r0 = tile * T48 + 8 * wave + sel;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vs[i] = vtable[min(r0 + 4 * i, nk - 1)];
+    }
+  };
+  uint32_t kchunk[2], kvx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // the row is 8*wave + 4i + sel: row & 15 == 8*(wave & 1) + 4i + sel, row & 7 == 4i + sel
+    kchunk[i] = kswz(8 * (wave & 1) + 4 * i + sel, lane & 15) * 16;
+    kvx[i] = kchunk[i] ^ (vswz48(4 * i + sel, lane & 15) * 16);
+  }
+  const uint32_t lds0 = lds_addr(smem) + 8 * wave * ROWB;
+  const char* kbase_s =
+      uniform_ptr((const char*)p.pool_k + (size_t)layer * p.layer_bytes + (size_t)g * p.geo.page_size * ROWB);
+  const char* vbase_s =
+      uniform_ptr((const char*)p.pool_v + (size_t)layer * p.layer_bytes + (size_t)g * p.geo.page_size * ROWB);
+  const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+  const int page_shift = p.geo.page_shift;
+  const uint32_t rmask = (uint32_t)(p.geo.page_size - 1) << 8;
+  auto koff = [&](uint32_t* off, const int32_t* vs) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t slot = (uint32_t)vs[i];
+      off[i] = __umul24(slot >> page_shift, page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
+    }
+  };
+  auto kissue = [&](int tile, const uint32_t* off) {
+    const uint32_t st = lds0 + (tile & 1) * T48_BYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+  };
+  auto vissue = [&](int tile, const uint32_t* off) {
+    const uint32_t st = lds0 + (2 + (tile & 1)) * T48_BYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+  };
+
+  // LDS read offsets within a stage: K fragment of step c (row r16 of key
+  // block kb, 16-byte chunk 4c + q; key block 1 adds 16 rows, which keep the
+  // swizzle); V^T fragment of dim block db (rows 4q + r16/4, 8 bytes at dim
+  // 16*db + 4*(r16 % 4); the second read adds 16 rows)
+  uint32_t krd[4], vrd[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) krd[c] = r16 * ROWB + kswz(r16, 4 * c + qd) * 16;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const uint32_t row = 4 * qd + (r16 >> 2);
+    const uint32_t dcol = 16 * db + 4 * (r16 & 3);
+    vrd[db] = row * ROWB + vswz48(row, dcol >> 3) * 16 + (dcol & 7) * 2;
+  }
+
+  // scores of a tile: s[kb][rb], keys 16*kb + 4q + i of the tile for query
+  // row r16 of row block rb
+  auto scores = [&](f32x4 (*s)[3], int tile) {
+    const char* st = smem + (tile & 1) * T48_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) s[kb][rb] = f32x4{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(st + krd[c] + kb * 16 * ROWB));
+#pragma unroll
+        for (int rb = 0; rb < 3; ++rb) s[kb][rb] = mfma16(kf, qf[rb][c], s[kb][rb]);
+      }
+  };
+  auto past_end = [&](int tile, int kb, int i) { return tile * T48 + 16 * kb + 4 * qd + i >= nk; };
+  auto mask = [&](f32x4 (*s)[3], int tile, float v) {
+    if (tile * T48 + T48 > nk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (past_end(tile, kb, i)) s[kb][rb][i] = v;
+    }
+  };
+  auto lane_sum = [&](f32x4 (*s)[3], int rb) -> float {
+    return ((s[0][rb][0] + s[0][rb][1]) + (s[0][rb][2] + s[0][rb][3])) +
+           ((s[1][rb][0] + s[1][rb][1]) + (s[1][rb][2] + s[1][rb][3]));
+  };
+  auto expsum = [&](f32x4 (*s)[3], int rb, float nm) -> float {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[kb][rb][i] = fast_exp2(fmaf(s[kb][rb][i], c2, nm));
+    return lane_sum(s, rb);
+  };
+  auto to_bf16 = [&](f32x4 (*s)[3], bf16x8* pw) {
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pw[rb][j] = (__bf16)s[j >> 2][rb][j & 3];
+  };
+  // exact step for row block rb: the tile's max of each row, the running max
+  // raised to it when larger (O and the row sum rescaled), then the weights
+  auto weigh_exact = [&](f32x4 (*s)[3], int rb) -> float {
+    float mr = fmaxf(fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3])),
+                     fmaxf(fmaxf(s[1][rb][0], s[1][rb][1]), fmaxf(s[1][rb][2], s[1][rb][3])));
+    const float mt = quad_max(mr) * c2;
+    if (mt > m[rb]) {
+      const float alpha = exp2f(m[rb] - mt);  // 0 while m is -inf (O and the sum are still 0)
+      lsum[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+      m[rb] = mt;
+    }
+    return expsum(s, rb, m[rb] == -INFINITY ? 0.f : -m[rb]);
+  };
+  // Weights of a freshly scored tile against the running max as it stands
+  // are kept when every lane's sum of them stays at most 2^8 (every weight
+  // does: a running max within 8 of the true one); otherwise the wave takes
+  // the exact step on scores recomputed from the tile, still in LDS.  Keys
+  // past the end of the list are zeroed after the exponentials.
+  auto weigh = [&](f32x4 (*s)[3], bf16x8* pw, int tile) {
+    float ls[3];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) ls[rb] = expsum(s, rb, -m[rb]);
+    if (tile * T48 + T48 > nk) {
+      mask(s, tile, 0.f);
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) ls[rb] = lane_sum(s, rb);
+    }
+    if (__builtin_amdgcn_ballot_w64(!(ls[0] <= 256.f) || !(ls[1] <= 256.f) || !(ls[2] <= 256.f)) != 0) {
+      scores(s, tile);
+      mask(s, tile, -INFINITY);
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) ls[rb] = weigh_exact(s, rb);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) lsum[rb] += ls[rb];
+    to_bf16(s, pw);
+  };
+  // the matrix work of an iteration: scores of tile t+1 (three MFMAs per K
+  // fragment) and P.V of tile t (three MFMAs per V^T fragment), a group of
+  // each in turn; reads two groups ahead
+  auto absorb_group = [&](const char* vst, const bf16x8* pc, int db) {
+    const char* vp = vst + vrd[db];
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 16 * ROWB));
+    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) o[db][rb] = mfma16(vf, pc[rb], o[db][rb]);
+  };
+  auto score_absorb = [&](f32x4 (*s)[3], int stile, const bf16x8* pc, int vtile) {
+    const char* st = smem + (stile & 1) * T48_BYTES;
+    const char* vst = smem + (2 + (vtile & 1)) * T48_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) s[kb][rb] = f32x4{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i >> 1, kb = i & 1;
+      const bf16x8 kf = as_bf16x8(*(const u32x4*)(st + krd[c] + kb * 16 * ROWB));
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) s[kb][rb] = mfma16(kf, qf[rb][c], s[kb][rb]);
+      absorb_group(vst, pc, i);
+    }
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 3, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kMfma, 3, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    }
+  };
+  f32x4 sn[2][3];
+  // iteration t: pc = P(t); pn receives P(t+1); oc = row offsets of tile t+1
+  // (its V load is issued here), on receives those of t+2; vs = slots of t+2
+  int32_t vs[2];
+  auto step = [&](int tile, const bf16x8* pc, bf16x8* pn, const uint32_t* oc, uint32_t* on) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1), V(t) and the slots of t+2 have landed
+    wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
+    if (tile + 2 < ntiles) {
+      koff(on, vs);
+      kissue(tile + 2, on);
+      if (tile + 3 < ntiles) sload(tile + 3, vs);
+    }
+    if (tile + 1 < ntiles) vissue(tile + 1, oc);
+    if (!live) return;
+    score_absorb(sn, tile + 1, pc, tile);
+    weigh(sn, pn, tile + 1);
+  };
+  auto last_step = [&](int tile, const bf16x8* pc) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): V(t) has landed
+    wg_barrier();
+    if (!live) return;
+    const char* vst = smem + (2 + (tile & 1)) * T48_BYTES;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) absorb_group(vst, pc, db);
+  };
+
+  bf16x8 pa[3], pb[3];
+  uint32_t oa[2], ob[2];
+  if (ntiles > 0) {
+    // the slots of tiles 0 and 1 in one round trip, both tiles' offsets,
+    // then the loads of K0, V0, K1 and the slots of tile 2
+    int32_t v1[2];
+    sload(0, vs);
+    if (ntiles > 1) sload(1, v1);
+    koff(ob, vs);
+    if (ntiles > 1) koff(oa, v1);
+    kissue(0, ob);
+    vissue(0, ob);
+    if (ntiles > 1) kissue(1, oa);
+    if (ntiles > 2) sload(2, vs);
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    wg_barrier();
+    if (live) {
+      scores(sn, 0);
+      mask(sn, 0, -INFINITY);
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) lsum[rb] += weigh_exact(sn, rb);
+      to_bf16(sn, pa);
+    }
+  }
+  for (int tile = 0; tile < ntiles - 1; tile += 2) {
+    step(tile, pa, pb, oa, ob);
+    if (tile + 2 < ntiles) step(tile + 1, pb, pa, ob, oa);
+  }
+  if (ntiles > 0) {
+    if (ntiles & 1) last_step(ntiles - 1, pa);
+    else last_step(ntiles - 1, pb);
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    const float lt = quad_sum(lsum[rb]);
+    if (!qvalid[rb]) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const size_t row = ((size_t)n * p.n_q + qrow[rb]) * p.n_q_heads + qhead[rb];
+    if (p.out) {
+      bf16_t* op = p.out + row * D + 4 * qd;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][rb][0] * inv, o[db][rb][1] * inv);
+        w[1] = pack_bf16x2(o[db][rb][2] * inv, o[db][rb][3] * inv);
+        *(u32x2*)(op + 16 * db) = w;
+      }
+    }
+    if (p.lse && qd == 0) p.lse[row] = lt > 0.f ? (m[rb] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // Read-slot attention of decode blocks whose requests share one affix
 // (Section 4.3 and Appendix C.1, with the single shared region of
 // Section 4.1).  A workgroup owns one (layer, query head) and four requests;
@@ -1535,7 +1902,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   const bool split = G == 0 && a.max_q <= 32;
   if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
   const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
-  const int RT = split ? 32 : 128;
+  const bool r48 = !split && rows >= kRows48MinRows;
+  const int RT = split ? 32 : (r48 ? 192 : 128);
   AttnP p{};
   p.q = (const bf16_t*)a.q;
   p.pool_k = (const bf16_t*)a.pool_k;
@@ -1568,6 +1936,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st, bool dry_run) {
   if (dry_run) return hipSuccess;
   dim3 grid(8 * p.per_xcd), block(256);
   if (split) hipLaunchKernelGGL(attn_split_mfma, grid, block, 0, st, p);
+  else if (r48) hipLaunchKernelGGL(attn_rows48_mfma, grid, block, 0, st, p);
   else hipLaunchKernelGGL(attn_rows_mfma, grid, block, 0, st, p);
   return hipGetLastError();
 }

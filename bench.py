@@ -402,6 +402,20 @@ def work_model(w, K):
 TRAFFIC_SOURCES = ("k_attn_mfma.hip", "k_tables.hip")   # the sources of the counted kernels
 
 
+def many_query_kernel(n_q_heads, n_kv_heads, max_q):
+    """The kernel a bf16, head_dim 128 read-slot or probe attention launch
+    takes, by the library's rule: the query heads of a KV-head group are
+    packed into a unit's rows when the group has several and the requests
+    have more than 32 rows or the group's rows reach 128; unpacked blocks of
+    at most 32 rows take the single pass; units of at least 384 rows take the
+    48-row kernel."""
+    G = n_q_heads // n_kv_heads
+    packed = G > 1 and (max_q > 32 or G * max_q >= 128)
+    if not packed and max_q <= 32:
+        return "attn_split_mfma"
+    return "attn_rows48_mfma" if (G * max_q if packed else max_q) >= 384 else "attn_rows_mfma"
+
+
 def code_digest(path):
     """sha256 of a kernel source without its comments and white space: it
     changes when the code changes, not when a comment does."""
@@ -618,9 +632,10 @@ def main():
     probe_ms_req = (stage_ms["probe_attention"] + stage_ms["probe_column_mass"] + stage_ms["topk_maps"]) / w.batch
     probe_tflops = wm["probe_flops"] / t_probe / 1e12
     traffic = measured_traffic(w.name)
-    roof = {"kernel": "attn_rows_mfma (probe attention, one launch for all layers)", "bound": "mfma",
+    probe_k = many_query_kernel(w.n_q_heads, w.n_kv_heads, S.n_rows)
+    roof = {"kernel": f"{probe_k} (probe attention, one launch for all layers)", "bound": "mfma",
             "achieved": probe_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get("attn_rows_mfma"),
+            "frac": probe_tflops / PEAK_BF16_TFLOPS, "traffic": traffic.get(probe_k),
             "traffic_unit": "HBM bytes per launch", "algorithmic_per_launch": wm["probe_flops"],
             "algorithmic_bytes_per_launch": wm["probe_bytes"]}
     mapped_gbs = wm["mapped_bytes"] / t_map / 1e9
@@ -628,8 +643,8 @@ def main():
     # ridge (2.5 PFLOP/s over 8 TB/s): it is then bound by the matrix units
     mapped_mfma = wm["mapped_flops"] / wm["mapped_bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mapped_mfma:
-        map_kernels = ("attn_rows_mfma",)   # packed query-head groups, single pass
-        roof_kernel = "read-slot attention, one call for all layers (attn_rows_mfma, query-head groups packed)"
+        map_kernels = (many_query_kernel(w.n_q_heads, w.n_kv_heads, w.block_len),)   # packed query-head groups
+        roof_kernel = f"read-slot attention, one call for all layers ({map_kernels[0]}, query-head groups packed)"
     elif w.batch < 2:
         # one request shares the affix with no other: the shared-affix call runs the single pass
         map_kernels = ("attn_split_mfma",)
@@ -637,7 +652,7 @@ def main():
     else:
         map_kernels = ("shared_plan_kernel", "attn_shared_mfma")
         roof_kernel = "read-slot attention, one shared-affix call for all layers (" + " + ".join(map_kernels) + ")"
-    map_traffic = [traffic.get(k) for k in (("attn_rows_mfma:read_slot",) if mapped_mfma else map_kernels)]
+    map_traffic = [traffic.get(k) for k in map_kernels]
     roof_mapped = {"kernel": roof_kernel, "bound": "mfma" if mapped_mfma else "hbm",
                    "achieved": mapped_tflops if mapped_mfma else mapped_gbs,
                    "peak": PEAK_BF16_TFLOPS if mapped_mfma else PEAK_HBM_GBS,

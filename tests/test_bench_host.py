@@ -87,7 +87,7 @@ def test_committed_traffic_record_matches_the_sources():
     rec = json.load(open(os.path.join(ROOT, "profiles", "pmc_traffic_llada-prefix-L4096-b16.json")))
     for f in bench.TRAFFIC_SOURCES:
         assert rec["code_sha256"][f] == bench.code_digest(os.path.join(ROOT, "attention_anchor_probe_amd", "csrc", f))
-    assert bench.measured_traffic("llada-prefix-L4096-b16")["attn_rows_mfma"] > 0
+    assert bench.measured_traffic("llada-prefix-L4096-b16")["attn_rows48_mfma"] > 0
 
 
 def test_more_than_one_gpu_is_refused():

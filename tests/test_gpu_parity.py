@@ -395,18 +395,19 @@ def test_store_attend_anchor_rates(hq, hkv, rate):
     128 fresh rows, two whole 64-key tiles, so no tile of the one-kernel path
     mixes fresh rows and pool slots; at 0.105 it has 129, one row into the
     next tile; with every affix position an anchor the storing requests read
-    nothing but their fresh rows."""
-    _store_attend_case("bf16", 128, hq, hkv, rate)
+    nothing but their fresh rows (an affix of 200, so that the 297 fresh
+    rows stay within the one kernel's limit)."""
+    _store_attend_case("bf16", 128, hq, hkv, rate, affix=200 if rate == 1.0 else 300)
 
 
-@pytest.mark.parametrize("anchors", [1439, 1440], ids=["1536-rows-one-kernel", "1537-rows-two-calls"])
+@pytest.mark.parametrize("anchors", [286, 287], ids=["383-rows-one-kernel", "384-rows-two-calls"])
 def test_store_attend_row_limit(anchors):
-    """The one kernel takes at most 1536 query rows per request (max_q_per_req);
-    one row more and the call makes the two calls of its definition.  Both
-    sides of that limit store the rows byte for byte and attend as the
-    oracle: request 0 recomputes 97 own positions plus its anchors, all of
-    them query rows."""
-    _store_attend_case("bf16", 128, 4, 4, anchors / 1800, affix=1800, expect_rows=anchors + 97)
+    """The one kernel takes at most 383 query rows per request (max_q_per_req);
+    one row more and the call makes the two calls of its definition (whose
+    attention is then the 48-row many-query kernel).  Both sides of that
+    limit store the rows byte for byte and attend as the oracle: request 0
+    recomputes 97 own positions plus its anchors, all of them query rows."""
+    _store_attend_case("bf16", 128, 4, 4, anchors / 400, affix=400, expect_rows=anchors + 97)
 
 
 def _store_attend_case(dtype, d, hq, hkv, rate, affix=300, expect_rows=None):
@@ -440,7 +441,7 @@ def _store_attend_case(dtype, d, hq, hkv, rate, affix=300, expect_rows=None):
         assert max(q_counts) == expect_rows
         one_kernel = A.acache_store_attend_workspace_bytes(k, v, B=w.batch, max_q_per_req=max(q_counts),
                                                            max_kv_per_req=w.T) > 0
-        assert one_kernel == (expect_rows <= 1536)
+        assert one_kernel == (expect_rows <= 383)
     out = torch.full_like(q, 7.0)
     lse = torch.empty(q.shape[:3], device=DEV)
     A.acache_store_attend(k, v, src_k, src_v, i32(rc_pos), i32(rc_slot), i32(src_off), q, i32(q_off), i32(read),

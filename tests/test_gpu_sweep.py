@@ -212,3 +212,73 @@ def test_probe_and_maps_sweep(seed):
     assert np.array_equal(read_slot.cpu().numpy(), np.concatenate(rd))
     assert np.array_equal(rc_pos.cpu().numpy()[:n_rc], np.concatenate(rp))
     assert np.array_equal(rc_slot.cpu().numpy()[:n_rc], np.concatenate(rs))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_many_query_sweep(seed):
+    """Units of at least 384 query rows (the many-query kernel with 48 rows
+    per wave): the read-slot attention of ragged query sets (some requests
+    with few or no rows, up to 1300) over ragged read tables (0, 1, 31-33
+    keys, up to 300; any slot of the pool), with one KV head serving 1-7
+    query heads, and the probe of up to 900 non-affix rows over an affix of
+    1-260 keys.  Against the oracle's definition of each (Section 4.3,
+    Appendix C.1; Section 3.2 Eq. 4)."""
+    rng = np.random.default_rng(7000 + seed)
+    hkv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 1, 2, 3, 4, 7]))
+    ps = int(rng.choice([4, 8, 16, 32]))
+    L = int(rng.integers(1, 260))
+    B = int(rng.integers(1, 5))
+    w = Workload(400 + seed, f"mqsweep{seed}", "bf16", int(rng.integers(1, 3)), G * hkv, hkv, 128,
+                 (("affix", L), ("gen", 40)), B, 0.3, page_size=ps, page_order="random")
+    K = A.acache_anchor_count(w.L, w.rate)
+    lay = gen.make_layout(w, K, seed)
+    k, v = gen.make_pool(w, lay, device=DEV, seed=seed)
+    nslot = lay.n_pages * w.page_size
+    scale = 1 / math.sqrt(w.head_dim)
+    # ragged query sets: one request holds at least 384 / G rows, so its
+    # units are many-query ones; the others hold 0 to 1300 rows
+    need = -(-384 // G)
+    q_counts = [int(rng.choice([0, int(rng.integers(1, 40)), int(rng.integers(need, 1300))])) for _ in range(B)]
+    q_counts[int(rng.integers(0, B))] = int(rng.integers(need, 1300))
+    q_off = np.concatenate([[0], np.cumsum(q_counts)]).astype(np.int32)
+    n_q = int(q_off[-1])
+    T = [int(rng.choice([0, 1, 31, 32, 33, int(rng.integers(2, 300))])) for _ in range(B)]
+    read = np.concatenate([rng.integers(0, nslot, t) for t in T] + [np.zeros(0)]).astype(np.int32)
+    kv_off = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    q = gen.make_rows(w, n_q, gen.S_QDEC, device=DEV, heads=w.n_q_heads, seed=seed)
+    torch.cuda.synchronize()
+    kh, vh, qh = map(np_of, (k, v, q))
+    out = torch.full_like(q, 7.0)
+    lse = torch.empty(q.shape[:3], device=DEV)
+    A.acache_mapped_attention(k, v, q, i32(q_off), i32(read), i32(kv_off), out, lse=lse,
+                              max_q_per_req=max(q_counts), max_kv_per_req=max(max(T), 1))
+    torch.cuda.synchronize()
+    for n in range(w.n_layers):
+        ref, rl = O.mapped_attention_layer(qh[n], kh[n], vh[n], q_off, read, kv_off, w.n_kv_heads, w.page_size,
+                                           scale)
+        o = out[n].float().cpu().numpy()
+        live = np.ones(n_q, bool)
+        for b, t in enumerate(T):
+            if t == 0:
+                live[q_off[b]:q_off[b + 1]] = False
+        ok, st = bf16_close(o[live], ref[live])
+        assert ok, (n, st)
+        assert (o[~live] == 0).all()
+        lg = lse[n].cpu().numpy()
+        assert np.isneginf(lg[~live]).all()
+        np.testing.assert_allclose(lg[live], rl[live], atol=1e-4)
+    # the probe of every non-affix row of a larger batch over the affix
+    pq = gen.make_rows(w, int(rng.integers(need, 900)), gen.S_QRC, device=DEV, heads=w.n_q_heads, seed=seed)
+    torch.cuda.synchronize()
+    pqh = np_of(pq)
+    o_aff = torch.empty_like(pq)
+    lse_aff = torch.empty(pq.shape[:3], device=DEV)
+    A.acache_probe_attention(k, v, pq, i32(lay.shared_slots), lse_aff, o_aff=o_aff)
+    torch.cuda.synchronize()
+    for n in range(w.n_layers):
+        o_ref, l_ref, _ = O.probe_layer(pqh[n], kh[n], vh[n], lay.shared_slots, w.page_size, w.n_kv_heads,
+                                        np.zeros(0, np.int64), np.zeros(2, np.int64), scale)
+        ok, st = bf16_close(o_aff[n].float().cpu().numpy(), o_ref)
+        assert ok, ("probe", n, st)
+        np.testing.assert_allclose(lse_aff[n].cpu().numpy(), l_ref, atol=1e-4)
