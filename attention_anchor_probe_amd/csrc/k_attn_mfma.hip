@@ -1157,10 +1157,13 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
       qrow[rb] = q0 + (qvalid[rb] ? lrow - j * nq : 0);
       qhead[rb] = g * p.gpack + j;
     }
+    // streaming loads: Q is read once, and the L2 is better kept for the
+    // affix tiles that every row tile of the head reads
     const bf16_t* qp = p.q + (((size_t)n * p.n_q + qrow[rb]) * p.n_q_heads + qhead[rb]) * D + 8 * qd;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      qf[rb][c] = qvalid[rb] ? as_bf16x8(ld16(qp + 32 * c)) : as_bf16x8(u32x4{0, 0, 0, 0});
+      qf[rb][c] = qvalid[rb] ? as_bf16x8(__builtin_nontemporal_load((const u32x4*)(qp + 32 * c)))
+                             : as_bf16x8(u32x4{0, 0, 0, 0});
   }
 
   float m[3] = {-INFINITY, -INFINITY, -INFINITY}, lsum[3] = {0.f, 0.f, 0.f};
