@@ -5,9 +5,12 @@
 //   table: the probe forward of the non-affix rows over the shared affix
 //   (Eq. 4 of "Affix Cache for Diffusion Large Language Models", Section 3.2)
 //   and the read-slot attention of Section 4.3 / Appendix C.1, in two shapes:
-//     attn_rows_mfma   a workgroup owns 128 query rows (32 per wave) and every
-//                      wave walks every key (probe, recompute-sized sets;
-//                      grouped query heads packed into the rows of a unit);
+//     attn_rows48_mfma a workgroup owns 192 query rows (48 per wave, three
+//                      16-row blocks on the 16x16x32 MFMA) and every wave
+//                      walks every key: units of at least 384 rows (probe,
+//                      recompute-sized sets, packed grouped query heads);
+//     attn_rows_mfma   the same with 128 query rows (32 per wave) for smaller
+//                      units (a decode block's packed query-head group);
 //     attn_store_rows_mfma  the same over a request's freshly recomputed
 //                      rows, read from their source while the same launch
 //                      stores them, and then its other keys
