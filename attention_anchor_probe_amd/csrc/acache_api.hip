@@ -580,14 +580,13 @@ struct StoreWs {
 };
 
 // Largest recompute set per request (query rows) that takes the one-kernel
-// path, whose attention is the 32-row tile loop.  Against the two calls with
-// the same tile loop, the one kernel saves the scatter's pass over the rows
-// but reads every source row once per row tile of its request: it measured
-// 2% faster at 1332 and 1536 rows per request and slower from 1741 rows up
-// (one query head per KV head, 12 layers, alternated on one box).  From
-// kRows48MinRows rows up the two calls' attention is the 48-row kernel, and
-// the two calls are faster (46.3 against 48.9 ms at 1332 rows, L=4096).
-constexpr int32_t kStoreOneKernelMaxRows = (int32_t)kRows48MinRows - 1;
+// path.  The one kernel saves the scatter's pass over the rows but reads
+// every source row once per row tile of its request.  With the 48-row kernel
+// in both forms (from kRows48MinRows rows), the one kernel measured 1.5-3%
+// faster than the two calls from 1332 to 2970 rows per request (12 layers,
+// stretched affixes of the L=4096 workload, alternated on one box) and 0.85%
+// slower at 5683 (L=16384, 32 requests).
+constexpr int32_t kStoreOneKernelMaxRows = 3072;
 
 StoreWs store_ws_layout(const acache_kv_pool* pool, int32_t B, int32_t max_q, int32_t max_kv) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };

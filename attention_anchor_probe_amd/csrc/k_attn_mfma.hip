@@ -1113,9 +1113,12 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
-  // two K stages then two V stages of 32-key tiles
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T48_BYTES];
+// STORE: the key list is the request's fresh rows (src_k / src_v) followed
+// by its other keys (priv_table), and the units of one query head per KV
+// head copy those rows of their (layer, KV head, request) to the pool, a
+// slice per row tile, as in rows_body<true>
+template <bool STORE>
+__device__ __forceinline__ void rows48_body(const AttnP& p, char* smem) {
   const int unit = xcd_unit(p.per_xcd);
   if (unit >= p.n_units) return;
   const bool packed = p.gpack > 1;
@@ -1130,14 +1133,55 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
   const int g = packed ? hu : hu / (p.n_q_heads / p.geo.n_kv_heads);
   const int layer = p.layer_begin + n;
   const int tid = threadIdx.x, lane = tid & 63;
+  if constexpr (STORE) {
+    // the q_tiles units of one query head per KV head copy the rows of their
+    // (layer, KV head, request) to the pool, one slice each, 16 bytes a
+    // thread and four rows' loads in flight before their stores
+    if (packed || hu % (p.n_q_heads / p.geo.n_kv_heads) == 0) {
+      const int s0 = p.src_offsets[b], s1 = p.src_offsets[b + 1];
+      const int per = (s1 - s0 + p.q_tiles - 1) / p.q_tiles;
+      const int c0 = s0 + t * per, c1 = min(s1, c0 + per);
+      const size_t row_stride = (size_t)p.geo.n_kv_heads * ROWB;
+      const size_t sbase = (size_t)n * p.n_src * row_stride + (size_t)g * ROWB;
+      const size_t dbase = (size_t)layer * p.layer_bytes + (size_t)g * p.geo.page_size * ROWB;
+      const size_t pg_bytes = (size_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
+      const int c = tid & 15;
+      for (int i0 = c0 + (tid >> 4); i0 < c1; i0 += 4 * 16) {
+        u32x4 kx[4], vx[4];
+        size_t dof[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = min(i0 + 16 * u, c1 - 1);  // rows past c1 repeat the last row's copy
+          const uint32_t slot = (uint32_t)p.src_slot[i];
+          const size_t so = sbase + (size_t)i * row_stride + c * 16;
+          dof[u] = dbase + (size_t)(slot >> p.geo.page_shift) * pg_bytes +
+                   (size_t)(slot & (p.geo.page_size - 1)) * ROWB + c * 16;
+          kx[u] = __builtin_nontemporal_load((const u32x4*)(p.src_k + so));
+          vx[u] = __builtin_nontemporal_load((const u32x4*)(p.src_v + so));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_nontemporal_store(kx[u], (u32x4*)(p.pool_kw + dof[u]));
+          __builtin_nontemporal_store(vx[u], (u32x4*)(p.pool_vw + dof[u]));
+        }
+      }
+    }
+  }
   int q0 = 0, q1 = p.n_q, k0 = 0, k1 = p.n_kv;
   if (p.q_offsets) { q0 = p.q_offsets[b]; q1 = p.q_offsets[b + 1]; }
-  if (p.kv_offsets) { k0 = p.kv_offsets[b]; k1 = p.kv_offsets[b + 1]; }
+  if constexpr (STORE) {
+    k1 = p.kv_counts[b];
+  } else if (p.kv_offsets) {
+    k0 = p.kv_offsets[b];
+    k1 = p.kv_offsets[b + 1];
+  }
   const int nq = q1 - q0;
   const int rows = packed ? p.gpack * nq : nq;
   const int rbase = t * 192;
   if (rbase >= rows) return;
-  const int nk = k1 - k0;
+  // STORE: keys 0 .. nf-1 are the fresh rows, keys nf .. nk-1 the table's
+  const int nf = STORE ? p.src_offsets[b + 1] - p.src_offsets[b] : 0;
+  const int nk = nf + k1 - k0;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, qd = lane >> 4;
@@ -1182,10 +1226,29 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
   // DMA instruction i covers rows 8*wave + 4i + lane/16, one 16-byte chunk
   // per lane
   const int sel = lane >> 4;
-  const int32_t* vtable = p.kv_table + k0;
-  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, nk * 4, 0x00020000);
+  const int32_t* vtable = STORE ? p.priv_table + (size_t)b * p.kv_stride : p.kv_table + k0;
+  const __amdgpu_buffer_rsrc_t trs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vtable, (short)0, (nk - nf) * 4, 0x00020000);
   const uint32_t trow = (uint32_t)(8 * wave + sel) * 4;
+  // the list position of the row this lane moves in DMA instruction i
+  auto key_of = [&](int tile, int i) { return min(tile * T48 + 8 * wave + sel + 4 * i, nk - 1); };
   auto sload = [&](int tile, int32_t* vs) {
+    if constexpr (STORE) {
+      // fresh rows need no slot; whole table tiles read it through the
+      // buffer resource shifted by nf; the tile across nf and the last
+      // partial tile read it per lane (keys below nf read entry 0, unused)
+      if (tile * T48 + T48 <= nf) {
+      } else if (tile * T48 >= nf && tile * T48 + T48 <= nk) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, (tile * T48 - nf) * 4 + 16 * i, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, (uint32_t)max(key_of(tile, i) - nf, 0) * 4, 0, 0);
+      }
+      return;
+    }
     if (tile * T48 + T48 <= nk) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) vs[i] = __builtin_amdgcn_raw_buffer_load_b32(trs, trow, tile * (T48 * 4) + 16 * i, 0);
@@ -1212,22 +1275,63 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
   const uint32_t page_bytes = (uint32_t)p.geo.n_kv_heads * p.geo.page_size * ROWB;
   const int page_shift = p.geo.page_shift;
   const uint32_t rmask = (uint32_t)(p.geo.page_size - 1) << 8;
-  auto koff = [&](uint32_t* off, const int32_t* vs) {
+  auto pool_off = [&](const int32_t* vs, int i) {
+    const uint32_t slot = (uint32_t)vs[i];
+    return __umul24(slot >> page_shift, page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
+  };
+  // STORE: a fresh row's offset in the source (row bytes and row count below
+  // 2^24, their product below 2^32)
+  const char* fkbase_s = STORE ? uniform_ptr(p.src_k + ((size_t)n * p.n_src + p.src_offsets[b]) *
+                                                           p.geo.n_kv_heads * ROWB + (size_t)g * ROWB)
+                               : nullptr;
+  const char* fvbase_s = STORE ? uniform_ptr(p.src_v + ((size_t)n * p.n_src + p.src_offsets[b]) *
+                                                           p.geo.n_kv_heads * ROWB + (size_t)g * ROWB)
+                               : nullptr;
+  const uint32_t fstride = (uint32_t)p.geo.n_kv_heads * ROWB;
+  auto fresh_off = [&](int tile, int i) { return __umul24((uint32_t)key_of(tile, i), fstride) + kchunk[i]; };
+  auto koff = [&](int tile, uint32_t* off, const int32_t* vs) {
+    if (!STORE || tile * T48 >= nf) {  // only table keys (uniform)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t slot = (uint32_t)vs[i];
-      off[i] = __umul24(slot >> page_shift, page_bytes) + (((slot << 8) & rmask) | kchunk[i]);
+      for (int i = 0; i < 2; ++i) off[i] = pool_off(vs, i);
+    } else if (tile * T48 + T48 <= nf) {  // only fresh rows (uniform)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) off[i] = fresh_off(tile, i);
+    } else {  // the one tile across nf: per lane
+#pragma unroll
+      for (int i = 0; i < 2; ++i) off[i] = key_of(tile, i) < nf ? fresh_off(tile, i) : pool_off(vs, i);
     }
   };
   auto kissue = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (tile & 1) * T48_BYTES;
+    if (!STORE || tile * T48 >= nf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      for (int i = 0; i < 2; ++i) dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+    } else if (tile * T48 + T48 <= nf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (key_of(tile, i) < nf) dma16s(fkbase_s, off[i], st + 4 * i * ROWB);
+        else dma16s(kbase_s, off[i], st + 4 * i * ROWB);
+      }
+    }
   };
   auto vissue = [&](int tile, const uint32_t* off) {
     const uint32_t st = lds0 + (2 + (tile & 1)) * T48_BYTES;
+    if (!STORE || tile * T48 >= nf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+      for (int i = 0; i < 2; ++i) dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    } else if (tile * T48 + T48 <= nf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16s(fvbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (key_of(tile, i) < nf) dma16s(fvbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+        else dma16s(vbase_s, off[i] ^ kvx[i], st + 4 * i * ROWB);
+      }
+    }
   };
 
   // LDS read offsets within a stage: K fragment of step c (row r16 of key
@@ -1373,7 +1477,7 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): K(t+1), V(t) and the slots of t+2 have landed
     wg_barrier();                        // ... in every wave; K(t) and V(t-1) are no longer read
     if (tile + 2 < ntiles) {
-      koff(on, vs);
+      koff(tile + 2, on, vs);
       kissue(tile + 2, on);
       if (tile + 3 < ntiles) sload(tile + 3, vs);
     }
@@ -1399,8 +1503,8 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
     int32_t v1[2];
     sload(0, vs);
     if (ntiles > 1) sload(1, v1);
-    koff(ob, vs);
-    if (ntiles > 1) koff(oa, v1);
+    koff(0, ob, vs);
+    if (ntiles > 1) koff(1, oa, v1);
     kissue(0, ob);
     vissue(0, ob);
     if (ntiles > 1) kissue(1, oa);
@@ -1442,6 +1546,17 @@ __global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
     }
     if (p.lse && qd == 0) p.lse[row] = lt > 0.f ? (m[rb] + log2f(lt)) * kLn2 : -INFINITY;
   }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_rows48_mfma(AttnP p) {
+  // two K stages then two V stages of 32-key tiles
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T48_BYTES];
+  rows48_body<false>(p, smem);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_store_rows48_mfma(AttnP p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T48_BYTES];
+  rows48_body<true>(p, smem);
 }
 
 // Read-slot attention of decode blocks whose requests share one affix
@@ -1951,6 +2066,8 @@ hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool d
   const int G = gqa_pack(a.n_q_heads, a.geo.n_kv_heads, a.max_q);
   if (G > 0 && (long long)G * a.n_q >= (1ll << 31)) return hipErrorInvalidValue;
   const long long rows = G > 0 ? (long long)G * a.max_q : a.max_q;
+  const bool r48 = rows >= kRows48MinRows;
+  const int RT = r48 ? 192 : 128;
   AttnP p{};
   p.q = (const bf16_t*)a.q;
   p.pool_k = (const bf16_t*)a.pool_k;
@@ -1960,7 +2077,7 @@ hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool d
   p.geo = a.geo;
   p.q_offsets = a.q_offsets;
   p.n_q = a.n_q;
-  const long long q_tiles = (rows + 127) / 128;
+  const long long q_tiles = (rows + RT - 1) / RT;
   if (q_tiles > (1ll << 30)) return hipErrorInvalidValue;
   p.q_tiles = (int)q_tiles;
   p.gpack = G;
@@ -1990,7 +2107,8 @@ hipError_t launch_attn_mfma_store(const StoreAttnArgs& a, hipStream_t st, bool d
   p.n_units = (int)units;
   p.per_xcd = (int)((units + 7) / 8);
   if (dry_run) return hipSuccess;
-  hipLaunchKernelGGL(attn_store_rows_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
+  if (r48) hipLaunchKernelGGL(attn_store_rows48_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(attn_store_rows_mfma, dim3(8 * p.per_xcd), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

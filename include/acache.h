@@ -349,7 +349,7 @@ int acache_mapped_attention_shared_noalloc(const acache_kv_pool* pool, const voi
  *  q, q_offsets, n_q, max_q_per_req, read_slot, kv_offsets, max_kv_per_req,
  *  out, lse    as for acache_mapped_attention.
  * For bf16 pools with head_dim 128, one query head per KV head and
- * max_q_per_req <= 383, one plan kernel and one attention kernel run: each
+ * max_q_per_req <= 3072, one plan kernel and one attention kernel run: each
  * request's rows attend to its source rows (read from k_src / v_src) and
  * then to its read list without its src_pos positions (read from the pool),
  * while the row tiles of each (layer, KV head, request) copy its source rows

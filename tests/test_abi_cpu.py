@@ -186,7 +186,7 @@ def test_store_attend_validation_and_workspace():
     assert ws(p, mq=0) == 0                       # no query rows: the scatter alone
     assert ws(pool(dtype=0, head_dim=64)) == 0    # other pools: the two calls of the definition
     assert ws(p, mkv=(1 << 18) + 1) == 0          # longer contexts: the two calls
-    assert ws(p, mq=383) > 0 and ws(p, mq=384) == 0     # larger recompute sets: the two calls
+    assert ws(p, mq=3072) > 0 and ws(p, mq=3073) == 0   # larger recompute sets: the two calls
     sa = lambda **kw: lib.acache_store_attend(
         ctypes.byref(kw.pop("pool", p)), kw.get("ks", FAKE), kw.get("vs", FAKE), FAKE, FAKE, kw.get("so", FAKE),
         kw.get("ns", 10), kw.get("q", FAKE), FAKE, kw.get("nq", 8), kw.get("mq", 8), FAKE, FAKE, kw.get("mkv", 100),
@@ -206,7 +206,7 @@ def test_store_attend_validation_and_workspace():
     # grouped query heads or more rows per request take the two calls, which
     # need no workspace: the first launch fails instead (EDEVICE, no GPU here)
     assert sa(hq=4, ws=None, wsb=0) == -8
-    assert sa(nq=384, mq=384, ws=None, wsb=0) == -8
+    assert sa(nq=3073, mq=3073, ws=None, wsb=0) == -8
 
 
 def test_size_limits_rejected_before_any_launch():

@@ -396,18 +396,22 @@ def test_store_attend_anchor_rates(hq, hkv, rate):
     mixes fresh rows and pool slots; at 0.105 it has 129, one row into the
     next tile; with every affix position an anchor the storing requests read
     nothing but their fresh rows (an affix of 200, so that the 297 fresh
-    rows stay within the one kernel's limit)."""
+    rows take the 32-row kernel; test_store_attend_row_limit covers the
+    48-row one)."""
     _store_attend_case("bf16", 128, hq, hkv, rate, affix=200 if rate == 1.0 else 300)
 
 
-@pytest.mark.parametrize("anchors", [286, 287], ids=["383-rows-one-kernel", "384-rows-two-calls"])
-def test_store_attend_row_limit(anchors):
-    """The one kernel takes at most 383 query rows per request (max_q_per_req);
-    one row more and the call makes the two calls of its definition (whose
-    attention is then the 48-row many-query kernel).  Both sides of that
-    limit store the rows byte for byte and attend as the oracle: request 0
-    recomputes 97 own positions plus its anchors, all of them query rows."""
-    _store_attend_case("bf16", 128, 4, 4, anchors / 400, affix=400, expect_rows=anchors + 97)
+@pytest.mark.parametrize("anchors,affix", [(286, 400), (287, 400), (2975, 3000), (2976, 3000)],
+                         ids=["383-rows-32-row-kernel", "384-rows-48-row-kernel", "3072-rows-48-row-kernel",
+                              "3073-rows-two-calls"])
+def test_store_attend_row_limit(anchors, affix):
+    """The one kernel takes at most 3072 query rows per request
+    (max_q_per_req): the 32-row tile loop below 384 rows, the 48-row kernel
+    from 384; one row more than 3072 and the call makes the two calls of its
+    definition.  Each side of both edges stores the rows byte for byte and
+    attends as the oracle: request 0 recomputes 97 own positions plus its
+    anchors, all of them query rows."""
+    _store_attend_case("bf16", 128, 4, 4, anchors / affix, affix=affix, expect_rows=anchors + 97)
 
 
 def _store_attend_case(dtype, d, hq, hkv, rate, affix=300, expect_rows=None):
@@ -441,7 +445,7 @@ def _store_attend_case(dtype, d, hq, hkv, rate, affix=300, expect_rows=None):
         assert max(q_counts) == expect_rows
         one_kernel = A.acache_store_attend_workspace_bytes(k, v, B=w.batch, max_q_per_req=max(q_counts),
                                                            max_kv_per_req=w.T) > 0
-        assert one_kernel == (expect_rows <= 383)
+        assert one_kernel == (expect_rows <= 3072)
     out = torch.full_like(q, 7.0)
     lse = torch.empty(q.shape[:3], device=DEV)
     A.acache_store_attend(k, v, src_k, src_v, i32(rc_pos), i32(rc_slot), i32(src_off), q, i32(q_off), i32(read),
